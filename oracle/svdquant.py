@@ -1,0 +1,300 @@
+"""Numpy oracle for the SVDQuant linear operator — test infrastructure only.
+
+Sources (cited by page title and section):
+  [P1] "SVDQuant Smoothing, Low-rank and Residual Quantization" (paperleet exercise),
+       sections "Functions / Return requirements" and "Formula and conventions".
+  [P4] "SVDQuant 参数配置流程指南" (msModelSlim SVDQuant usage guide), step 2
+       (recommended YAML: MXFP4, per_block, symmetric, minmax for act and weight).
+  [P5] "Contraction-Gauge Preconditioning for Quantized Matrix Multiplication",
+       abstract: the product identity AB = (AT)(T^-1 B).
+
+Precision conventions (readings where the pages are silent; each one is listed
+in the design notes):
+  * elementwise steps run in IEEE binary32 with subnormals, no contraction
+    (numpy float32 ops), or binary64 for float64 inputs;
+  * bf16 is a storage type: values are upcast exactly to float32, the step runs
+    in float32, the result is rounded once (RNE) to bf16;
+  * reference products and sums run in float64.
+
+Every function here is a plain transcription of a definition; nothing is
+blocked, fused or reordered. Tensors are numpy arrays; bf16 tensors are float32
+arrays holding bf16-representable values.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "bf16", "f64")
+MX_BLOCK = 32
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+# --------------------------------------------------------------------------- dtype rounding
+def round_to_format(v, mant_bits: int, emin: int) -> np.ndarray:
+    """Round float64 values to a binary format with ``mant_bits`` fraction bits and
+    minimum normal exponent ``emin`` (round half to even, gradual underflow).
+
+    The spacing of representable numbers around v is 2^(max(floor(log2|v|), emin) - mant_bits);
+    v / spacing is an exact power-of-two rescaling, so rint() performs the one rounding.
+    Overflow is not handled (inputs are finite and far from the format's maximum).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, E = np.frexp(v)  # v = f * 2^E with 0.5 <= |f| < 1, so floor(log2|v|) = E - 1
+    e = np.maximum(E - 1, emin)
+    q = np.ldexp(np.ones_like(v), e - mant_bits)
+    return np.rint(v / q) * q
+
+
+def to_dtype(v, dtype: str) -> np.ndarray:
+    """D(.): round to the storage dtype ("f32" or "bf16" -> float32 array, "f64" -> float64)."""
+    if dtype == "f64":
+        return np.asarray(v, dtype=np.float64)
+    if dtype == "f32":
+        return np.asarray(v, dtype=np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return round_to_format(v, 7, -126).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _work(dtype: str):
+    """Arithmetic type of elementwise steps: float64 for f64 tensors, float32 otherwise."""
+    return np.float64 if dtype == "f64" else np.float32
+
+
+# --------------------------------------------------------------------------- validation
+def check_smoothing(x, weight, scale) -> None:
+    """[P1] _check_smoothing: nonempty x[B,M], weight[M,N], positive finite scale[M]."""
+    x, weight, scale = np.asarray(x), np.asarray(weight), np.asarray(scale)
+    if x.ndim != 2 or weight.ndim != 2 or scale.ndim != 1:
+        raise ValueError("x and weight must be 2-D and scale 1-D")
+    if x.size == 0 or weight.size == 0 or scale.size == 0:
+        raise ValueError("empty input")
+    if not (x.shape[1] == weight.shape[0] == scale.shape[0]):
+        raise ValueError("input-channel sizes of x, weight and scale differ")
+    s = scale.astype(np.float64)
+    if not np.all(np.isfinite(s)) or not np.all(s > 0):
+        raise ValueError("scale must be positive and finite")
+
+
+def check_rank(weight, rank) -> None:
+    """[P1] _check_rank: weight is a matrix and rank a Python int in [0, min(M, N)]."""
+    weight = np.asarray(weight)
+    if weight.ndim != 2:
+        raise ValueError("weight must be a matrix")
+    if isinstance(rank, bool) or not isinstance(rank, int):
+        raise ValueError("rank must be a Python int")
+    if rank < 0 or rank > min(weight.shape):
+        raise ValueError("rank out of range")
+
+
+def check_bits(bits) -> None:
+    """[P1] "Formula and conventions" item 3: 2 <= bits <= 8."""
+    if isinstance(bits, bool) or not isinstance(bits, int) or not 2 <= bits <= 8:
+        raise ValueError("bits must be an int in [2, 8]")
+
+
+# --------------------------------------------------------------------------- smoothing
+def smooth_activations(x, scale, dtype: str) -> np.ndarray:
+    """Activation half of [P1] smooth_inputs: xs = D(x / scale[None, :])."""
+    w = _work(dtype)
+    return to_dtype(np.asarray(x, w) / np.asarray(scale, w)[None, :], dtype)
+
+
+def smooth_weight(weight, scale, dtype: str) -> np.ndarray:
+    """Weight half of [P1] smooth_inputs: ws = D(scale[:, None] * weight)."""
+    w = _work(dtype)
+    return to_dtype(np.asarray(scale, w)[:, None] * np.asarray(weight, w), dtype)
+
+
+def smooth_inputs(x, weight, scale, dtype: str):
+    """[P1] smooth_inputs / "Formula and conventions" item 1: (x/scale, scale[:,None]*weight).
+
+    Moving the per-channel factor from x into W leaves the product unchanged
+    ([P5]'s identity with T = diag(1/scale)).
+    """
+    check_smoothing(x, weight, scale)
+    return smooth_activations(x, scale, dtype), smooth_weight(weight, scale, dtype)
+
+
+# --------------------------------------------------------------------------- low-rank split
+def residual_of(weight, left, right, dtype: str) -> np.ndarray:
+    """R = D(weight - left @ right), the product taken in float64 from the stored factors."""
+    w64 = np.asarray(weight, np.float64)
+    prod = np.asarray(left, np.float64) @ np.asarray(right, np.float64)
+    return to_dtype(w64 - prod, dtype)
+
+
+def split_weight(weight, rank: int, dtype: str):
+    """[P1] split_weight / "Formula and conventions" item 2.
+
+    Truncated SVD in float64: left = D(U_r diag(sigma_r)), right = D(V_r^T),
+    residual = D(weight - left @ right). rank 0 gives [M,0] and [0,N] factors
+    and the weight itself as residual.
+    """
+    check_rank(weight, rank)
+    w64 = np.asarray(weight, np.float64)
+    M, N = w64.shape
+    if rank == 0:
+        left = np.zeros((M, 0), np.float64)
+        right = np.zeros((0, N), np.float64)
+    else:
+        U, s, Vt = np.linalg.svd(w64, full_matrices=False)
+        left = U[:, :rank] * s[:rank]
+        right = Vt[:rank]
+    left = to_dtype(left, dtype)
+    right = to_dtype(right, dtype)
+    return left, right, residual_of(weight, left, right, dtype)
+
+
+# --------------------------------------------------------------------------- per-tensor INT
+def quantize_int(z, bits: int, dtype: str = "f32"):
+    """[P1] fake_quantize rule: one symmetric scale for the whole tensor.
+
+    qmax = 2^(bits-1) - 1, s = max|z| / qmax, codes = clamp(round_half_even(z / s), -qmax, qmax).
+    Divisions are IEEE in the working precision. An all-zero tensor gives s = 0
+    and zero codes. Returns (codes int32, s).
+    """
+    check_bits(bits)
+    w = _work(dtype)
+    qmax = 2 ** (bits - 1) - 1
+    z = np.asarray(z, w)
+    a = np.max(np.abs(z)) if z.size else w(0)
+    if a == 0:
+        return np.zeros(z.shape, np.int32), w(0)
+    s = w(a) / w(qmax)
+    codes = np.clip(np.rint(z / s), -qmax, qmax).astype(np.int32)
+    return codes, w(s)
+
+
+def fake_quantize(z, bits: int, dtype: str) -> np.ndarray:
+    """[P1] fake_quantize: dequantised values D(s * codes), same shape as z."""
+    codes, s = quantize_int(z, bits, dtype)
+    w = _work(dtype)
+    return to_dtype(w(s) * codes.astype(w), dtype)
+
+
+# --------------------------------------------------------------------------- per-block MXFP4
+def mx_block_exponent(amax) -> np.ndarray:
+    """Shared exponent of an MXFP4 block from its max magnitude (minmax, [P4] step 2).
+
+    e is the smallest integer with amax <= 6 * 2^e (6 = largest E2M1 magnitude), so the
+    block maximum never saturates; e is clamped to the E8M0 range [-127, 127] and an
+    all-zero block takes -127.  With amax = f * 2^E (0.5 <= f < 1): 6 * 2^(E-4) < amax < 6 * 2^(E-2),
+    so the answer is E-3 when amax <= 6 * 2^(E-3) and E-2 otherwise.
+    """
+    a = np.asarray(amax, np.float64)
+    _, E = np.frexp(a)
+    e = np.where(a <= 6.0 * np.ldexp(1.0, E - 3), E - 3, E - 2)
+    e = np.where(a == 0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def e2m1_code(v) -> np.ndarray:
+    """4-bit E2M1 code of v: magnitude rounded to the nearest of {0,.5,1,1.5,2,3,4,6}
+    (codes 0..7), a tie going to the even code; bit 3 = sign bit of v (so -0 -> 8).
+    Magnitudes above 6 take code 7."""
+    v = np.asarray(v, np.float64)
+    d = np.abs(np.abs(v)[..., None] - E2M1_GRID)  # distance to each grid point
+    is_min = d == d.min(axis=-1, keepdims=True)
+    even_min = is_min & (np.arange(8) % 2 == 0)
+    idx = np.where(even_min.any(axis=-1), np.argmax(even_min, axis=-1), np.argmax(is_min, axis=-1))
+    return (idx | (np.signbit(v).astype(np.int64) << 3)).astype(np.uint8)
+
+
+def quantize_mx(z, block: int = MX_BLOCK):
+    """MXFP4 quantisation of z[rows, K] along K in blocks of ``block`` (the last one may be short).
+
+    Per block: e from the block max (mx_block_exponent), v = z * 2^-e (exact), code = e2m1_code(v).
+    Returns (codes uint8 [rows, K] in 0..15, scale bytes uint8 [rows, ceil(K/block)] = e + 127).
+    """
+    z = np.asarray(z, np.float64)
+    rows, K = z.shape
+    nb = -(-K // block)
+    codes = np.zeros((rows, K), np.uint8)
+    sbytes = np.zeros((rows, nb), np.uint8)
+    for j in range(nb):
+        blk = z[:, j * block:(j + 1) * block]
+        e = mx_block_exponent(np.max(np.abs(blk), axis=1))
+        v = blk * np.ldexp(1.0, -e)[:, None]
+        codes[:, j * block:(j + 1) * block] = e2m1_code(v)
+        sbytes[:, j] = (e + 127).astype(np.uint8)
+    return codes, sbytes
+
+
+def dequant_mx(codes, sbytes, block: int = MX_BLOCK) -> np.ndarray:
+    """Exact float64 values of MXFP4 codes: grid[code & 7] * (-1)^bit3 * 2^(byte - 127)."""
+    codes = np.asarray(codes)
+    mag = E2M1_GRID[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    e = np.repeat(np.asarray(sbytes, np.int64) - 127, block, axis=1)[:, : codes.shape[1]]
+    return val * np.ldexp(1.0, e)
+
+
+# --------------------------------------------------------------------------- packed layouts
+def pack_nibbles(codes4) -> np.ndarray:
+    """Pack 4-bit codes [rows, K] two per byte, even k in the low nibble: [rows, ceil(K/2)]."""
+    c = np.asarray(codes4).astype(np.uint8) & 0xF
+    rows, K = c.shape
+    if K % 2:
+        c = np.concatenate([c, np.zeros((rows, 1), np.uint8)], axis=1)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def pack_int_codes(codes, bits: int) -> np.ndarray:
+    """Canonical INT code layout: 4-bit two's-complement nibbles for bits <= 4, else int8 bytes."""
+    codes = np.asarray(codes, np.int64)
+    if bits <= 4:
+        return pack_nibbles(codes & 0xF)
+    return codes.astype(np.int8).view(np.uint8)
+
+
+# --------------------------------------------------------------------------- the operator
+def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str) -> np.ndarray:
+    """[P1] "Formula and conventions" item 3, Y = (X^ L1) L2 + Q(X^) Q(R), in float64.
+
+    X^ = D(x/scale). The low-rank branch uses the unquantised X^ and the stored
+    factors; only R is quantised on the weight side. fmt "int": per-tensor INT
+    (s_x * s_R * integer product, exact); fmt "mx": MXFP4 along K for X^ rows and
+    R columns ([P4] per_block), the product of exactly dequantised values.
+    """
+    xs = smooth_activations(x, scale, dtype)
+    low = (np.asarray(xs, np.float64) @ np.asarray(left, np.float64)) @ np.asarray(right, np.float64)
+    if fmt == "int":
+        cx, sx = quantize_int(xs, bits, dtype)
+        cr, sr = quantize_int(residual, bits, dtype)
+        res = float(sx) * float(sr) * (cx.astype(np.float64) @ cr.astype(np.float64))
+    elif fmt == "mx":
+        if bits != 4:
+            raise ValueError("MXFP4 uses 4-bit codes")
+        cx, bx = quantize_mx(xs)
+        cr, br = quantize_mx(np.asarray(residual).T)
+        res = dequant_mx(cx, bx) @ dequant_mx(cr, br).T
+    else:
+        raise ValueError(f"unknown format {fmt!r}")
+    return low + res
+
+
+def svdquant_linear(x, weight, scale, rank: int, bits: int = 4):
+    """[P1] svdquant_linear on float32/float64 inputs: smooth, split the smoothed weight,
+    Y = (X^ L1) L2 + fake_quantize(X^) @ fake_quantize(R), returned in the input dtype."""
+    x = np.asarray(x)
+    dtype = "f64" if x.dtype == np.float64 else "f32"
+    check_smoothing(x, weight, scale)
+    check_rank(weight, rank)
+    check_bits(bits)
+    xs, ws = smooth_inputs(x, weight, scale, dtype)
+    left, right, res = split_weight(ws, rank, dtype)
+    qx = np.asarray(fake_quantize(xs, bits, dtype), np.float64)
+    qr = np.asarray(fake_quantize(res, bits, dtype), np.float64)
+    y = (np.asarray(xs, np.float64) @ np.asarray(left, np.float64)) @ np.asarray(right, np.float64) + qx @ qr
+    return to_dtype(y, dtype)
+
+
+def rel_fro(y, ref) -> float:
+    """Relative Frobenius error ||y - ref||_F / ||ref||_F (float64)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(y - ref) / den) if den > 0 else float(np.linalg.norm(y))
