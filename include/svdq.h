@@ -1,0 +1,216 @@
+/*
+ * svdq.h — C ABI of the SVDQuant linear operator for AMD Instinct MI355X (gfx950).
+ *
+ *   Y = (X^ L1) L2 + Q(X^) Q(R),   X^ = x / scale,   L1 L2 = rank-r truncated SVD of
+ *   scale[:,None] * W,   R = scale[:,None] * W - L1 L2.
+ *
+ * Sources, cited by page title and section:
+ *   [EX]  "SVDQuant Smoothing, Low-rank and Residual Quantization" (paperleet exercise):
+ *         "Functions / Return requirements" (smooth_inputs, split_weight, svdquant_linear,
+ *         fake_quantize, _check_smoothing, _check_rank) and "Formula and conventions" items 1-3.
+ *   [FI]  "flashinfer.gemm.svdquant_linear" (API page): the three-step chain (smooth+quantise,
+ *         down-projection GEMM, residual GEMM with low-rank epilogue), offline preparation by
+ *         the caller, rank a multiple of 32.
+ *   [MS]  "SVDQuant 参数配置流程指南" (msModelSlim usage guide), step 2: MXFP4 per-block
+ *         symmetric minmax quantisation of activations and weights, rank 32.
+ *
+ * Conventions for every call
+ *   - Layout: x is [B, M], weight is [M, N] (not the transposed Linear layout), scale is [M],
+ *     Y is [B, N]. Matrices are row-major with an explicit row stride in ELEMENTS; the
+ *     elementwise calls also take a column stride (strided inputs, [EX] "Formula and
+ *     conventions", last paragraph).
+ *   - dtype: SVDQ_F32 or SVDQ_BF16 for x, weight and every dtype-typed output (they share one
+ *     dtype); scale is always float32. float64 is rejected with SVDQ_EDTYPE.
+ *   - Ownership: the caller owns every buffer (inputs, outputs, prepared weights, workspace).
+ *     The library never allocates device memory and never writes an input. Outputs must not
+ *     overlap inputs.
+ *   - Device calls take a hipStream_t, only enqueue work on it (asynchronous, stream-ordered)
+ *     and return; faults inside kernels surface at the caller's next synchronisation.
+ *   - Errors: every call returns an svdq_status; svdq_last_error() gives a message for the
+ *     last failing call on the calling thread. Invalid arguments ([EX] _check_smoothing,
+ *     _check_rank, 2 <= bits <= 8) return SVDQ_EINVAL before any work is enqueued.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* svdq_stream_t; /* the same handle as hipStream_t */
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_EINVAL = 1,       /* invalid shape, stride, rank, bits, scale or buffer size */
+  SVDQ_EDTYPE = 2,       /* unsupported dtype (e.g. float64) */
+  SVDQ_EUNSUPPORTED = 3, /* valid request this build does not implement */
+  SVDQ_EHIP = 4          /* a HIP runtime call failed (launch error, bad device pointer) */
+} svdq_status;
+
+typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1, SVDQ_F64 = 2 } svdq_dtype;
+
+typedef enum {
+  SVDQ_FMT_INT = 0, /* per-tensor symmetric INT, 2 <= bits <= 8 ([EX] fake_quantize rule) */
+  SVDQ_FMT_MX = 1   /* MXFP4: E2M1 codes, one E8M0 scale per 32 elements along K ([MS] step 2) */
+} svdq_format;
+
+/* Message of the last failing call on this thread ("" if none). Never NULL. */
+const char* svdq_last_error(void);
+
+/* Library version string, e.g. "svdq 0.1 gfx950". */
+const char* svdq_version(void);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_smooth_inputs — [EX] smooth_inputs / "Formula and conventions" item 1.
+ *   xs[b,m] = D(x[b,m] / scale[m]),  ws[m,n] = D(scale[m] * weight[m,n]),
+ * with IEEE binary32 division / multiplication and D = rounding to dtype (RNE for bf16).
+ * xs @ ws equals x @ weight up to that rounding. Device pointers.
+ *   x: [B,M] with strides (sxb, sxm); weight: [M,N] with strides (swm, swn); scale: [M] f32,
+ *   contiguous. xs_out: [B,M] row stride ldxs (unit column stride); ws_out: [M,N] row
+ *   stride ldws. Either of (x, xs_out) or (weight, ws_out) may be NULL to skip that half.
+ * Errors: EINVAL (empty, bad stride), EDTYPE. Scale positivity is the caller's contract
+ *   on the device path (checking it would need a device read); svdq_check_smoothing
+ *   validates a host copy.
+ * ------------------------------------------------------------------------------------ */
+int svdq_smooth_inputs(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t sxm,
+                       const void* weight, int64_t N, int64_t swm, int64_t swn,
+                       const float* scale, int dtype,
+                       void* xs_out, int64_t ldxs, void* ws_out, int64_t ldws,
+                       svdq_stream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_check_smoothing / svdq_check_rank — [EX] _check_smoothing and _check_rank on host
+ * data: B, M, N >= 1, every scale[m] positive and finite, 0 <= rank <= min(M,N).
+ * Return SVDQ_OK or SVDQ_EINVAL with a message.
+ * ------------------------------------------------------------------------------------ */
+int svdq_check_smoothing(int64_t B, int64_t M, int64_t Mw, int64_t Ms, int64_t N, const float* scale_host);
+int svdq_check_rank(int64_t M, int64_t N, int64_t rank);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_split_weight — [EX] split_weight / "Formula and conventions" item 2. HOST call.
+ * Truncated SVD of weight [M,N] (host, row stride ldw, dtype) computed in float64 by the
+ * library (one-sided Jacobi for small matrices, randomized subspace iteration with a
+ * Rayleigh-Ritz step for large ones; no LAPACK):
+ *   left  = D(U_r diag(sigma_r))  [M, r] row-major contiguous,
+ *   right = D(V_r^T)              [r, N] row-major contiguous,
+ *   residual = D(weight - left @ right) [M, N] row-major contiguous, the product taken in
+ *   float64 from the stored (rounded) factors.
+ * rank 0 writes nothing to left/right (they may be NULL) and copies weight to residual.
+ * Singular-vector signs are free; the result is deterministic for a given input.
+ * Errors: EINVAL (rank out of [0, min(M,N)], empty), EDTYPE.
+ * ------------------------------------------------------------------------------------ */
+int svdq_split_weight(const void* weight, int64_t M, int64_t N, int64_t ldw, int dtype, int64_t rank,
+                      void* left, void* right, void* residual);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_fake_quantize — [EX] fake_quantize / "Formula and conventions" item 3. Device call.
+ * One scale per tensor: qmax = 2^(bits-1)-1, s = max|z| / qmax (binary32 division),
+ * out = D(s * clamp(round_half_even(z / s), -qmax, qmax)); an all-zero tensor gives zeros.
+ *   z: [rows, cols] with strides (szr, szc); out: [rows, cols] row stride ldo.
+ *   workspace: device scratch of at least svdq_fake_quantize_workspace(rows, cols) bytes
+ *   (per-block partial maxima; no initialisation needed).
+ *   s_out: optional device float* receiving s (may be NULL).
+ * Errors: EINVAL (bits outside [2,8], empty, workspace too small), EDTYPE.
+ * ------------------------------------------------------------------------------------ */
+size_t svdq_fake_quantize_workspace(int64_t rows, int64_t cols);
+int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, int dtype,
+                       int bits, void* out, int64_t ldo, float* s_out,
+                       void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * Prepared weights ([FI]: the per-layer invariants are prepared offline by the caller).
+ * One contiguous blob, built on the host by svdq_prepare, copied to the device by the
+ * caller, and passed to svdq_linear. Sections (byte offsets from svdq_prepared_layout,
+ * each 256-byte aligned), with Kp = M rounded up to 256, Np = N rounded up to 256 and
+ * rp = rank rounded up to 32 (zero padding is exact: padded codes and factors are 0):
+ *   SVDQ_SEC_SCALE   float32 [M]       the smoothing scale (divisor of x)
+ *   SVDQ_SEC_RCODES  uint8 [Np, Kp/2]  R^T codes, K-contiguous per output column n:
+ *                    two 4-bit codes per byte, even k in the low nibble (MX: E2M1;
+ *                    INT bits<=4: two's-complement nibbles) — or int8 [Np, Kp] for INT bits>4
+ *   SVDQ_SEC_RSCALES MX: uint8 [Np, Kp/32] E8M0 bytes (e + 127) per 32-block of column n;
+ *                    INT: one float32 s_R
+ *   SVDQ_SEC_L1T     dtype [rp, Kp]    L1^T (down-projection factor, transposed)
+ *   SVDQ_SEC_L2T     dtype [Np, rp]    L2^T (up-projection factor, transposed)
+ * ------------------------------------------------------------------------------------ */
+enum {
+  SVDQ_SEC_SCALE = 0,
+  SVDQ_SEC_RCODES = 1,
+  SVDQ_SEC_RSCALES = 2,
+  SVDQ_SEC_L1T = 3,
+  SVDQ_SEC_L2T = 4,
+  SVDQ_SEC_END = 5, /* offsets[SVDQ_SEC_END] = total blob bytes */
+  SVDQ_NSEC = 6
+};
+
+/* Offsets of every section and the total size. Errors: EINVAL, EDTYPE. */
+int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
+                         int64_t offsets[SVDQ_NSEC]);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_prepare — one-time HOST preparation ([EX] svdquant_linear: smooth, then split the
+ * smoothed weight, quantise the residual; [MS] iter_smooth -> svd_res -> linear_quant):
+ *   ws = D(scale[:,None] * weight)  (binary32 product, rounded to dtype)
+ *   (left, right, residual) = svdq_split_weight(ws, rank)
+ *   residual quantised per tensor (INT: s_R = max|R|/qmax, codes) or per 32-block along M
+ *   for each column n (MX), then packed into the blob layout above.
+ *   weight [M,N] host row stride ldw, scale [M] host float32, blob_host of
+ *   offsets[SVDQ_SEC_END] bytes. left_out [M,rank], right_out [rank,N], residual_out [M,N]
+ *   (host, dtype, contiguous) optionally receive the exact factors and R used (may be NULL).
+ * Errors: EINVAL ([EX] _check_smoothing/_check_rank cases, bits, MX with bits != 4), EDTYPE.
+ * ------------------------------------------------------------------------------------ */
+int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
+                 int64_t rank, int fmt, int bits, int dtype, void* blob_host,
+                 void* left_out, void* right_out, void* residual_out);
+
+/* --------------------------------------------------------------------------------------
+ * Workspace of svdq_linear / svdq_quantize_activations: device scratch the caller
+ * allocates once (any contents; nothing needs zeroing) and may reuse across calls that are
+ * ordered on one stream. Holds activation codes [B, Kp/2] (int8 [B,Kp] for INT bits>4),
+ * MX scales [B, Kp/32], the down-projection [B, rp], its split-K partials and the
+ * per-tensor INT maxima. Errors: EINVAL, EDTYPE.
+ * ------------------------------------------------------------------------------------ */
+int svdq_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
+                         size_t* bytes_out);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_linear — the per-call hot path ([EX] svdquant_linear, Eq. Y = (X^L1)L2 + Q(X^)Q(R);
+ * kernel split after [FI]'s three-step chain). Device call:
+ *   (a) X^ = D(x / scale) (binary32 IEEE division), quantised per tensor (INT: s_x from the
+ *       global max |X^|) or per 32-block along M (MX), codes packed; fused with
+ *   (b) down = X^ L1 (the low-rank branch uses the unquantised X^), fp32 accumulation,
+ *       stored in dtype;
+ *   (c) Y = D( Q(X^) Q(R) + down L2 ), the residual product on int8 (INT) or block-scaled
+ *       FP4 (MX) matrix cores with fp32 (or exact int32) accumulation, the dequant scales
+ *       and the up-projection applied in the epilogue.
+ *   x: device [B, M] dtype with row stride ldx (unit column stride); blob: device copy of
+ *   svdq_prepare's output for the same (M, N, rank, fmt, bits, dtype); y: device [B, N]
+ *   dtype with row stride ldy; workspace: >= svdq_workspace_bytes(...).
+ * Errors: EINVAL (shape, stride, workspace), EDTYPE, EHIP (launch failure).
+ * ------------------------------------------------------------------------------------ */
+int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob,
+                int64_t N, int64_t rank, int fmt, int bits, int dtype,
+                void* y, int64_t ldy, void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * svdq_quantize_activations — step (a) alone, for bit-exact checks ([EX] "Formula and
+ * conventions" item 3 for INT; [MS] step 2 for MX). Device call.
+ *   x [B,M] dtype row stride ldx; scale [M] f32 device.
+ *   codes_out: [B, ldc] bytes; row b holds ceil(M/2) packed 4-bit codes (even m in the low
+ *   nibble; INT bits<=4 two's complement, MX E2M1) or M int8 codes for INT bits>4; bytes up
+ *   to the padded width Kp/2 (Kp) are written with zero codes, so ldc >= Kp/2 (Kp).
+ *   scales_out (MX): [B, lds] E8M0 bytes, ceil(M/32) meaningful per row, lds >= Kp/32.
+ *   sx_out (INT): device float* receiving s_x. Unused outputs may be NULL.
+ *   workspace: >= svdq_workspace_bytes(B, M, 1, 0, fmt, bits, dtype).
+ * ------------------------------------------------------------------------------------ */
+int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, const float* scale,
+                              int fmt, int bits, int dtype,
+                              void* codes_out, int64_t ldc, void* scales_out, int64_t lds, float* sx_out,
+                              void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */

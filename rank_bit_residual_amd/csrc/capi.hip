@@ -1,0 +1,262 @@
+// Device-side C ABI of libsvdq: argument validation, launch plans, workspace layout and the
+// launch sequences of svdq_linear (steps a+b, optional split-K reduction, c),
+// svdq_quantize_activations, svdq_fake_quantize and svdq_smooth_inputs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <string>
+
+#include "launch.h"
+#include "svdq_internal.h"
+
+namespace svdq {
+
+LaunchPlan make_plan(const Dims& d, int64_t B) {
+  LaunchPlan p;
+  p.B = B;
+  p.row_blocks = (int)ceil_div(B, 16);
+  // Split K across blocks when there are few row blocks, so that ~512 blocks stream L1^T.
+  const int64_t max_chunks = std::max<int64_t>(1, d.Kp / 512);
+  const int64_t want = std::max<int64_t>(1, ceil_div(512, p.row_blocks));
+  const int64_t chunks = std::min(max_chunks, want);
+  p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
+  p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
+  p.amax_blocks = (int)std::min<int64_t>(B, 1024);
+  return p;
+}
+
+void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]) {
+  int64_t o = 0;
+  auto sec = [&](int id, int64_t bytes) {
+    off[id] = o;
+    o = round_up(o + bytes, kAlign);
+  };
+  const int64_t B = p.B;
+  sec(WS_CODES, B * d.code_row_bytes());
+  sec(WS_SCALES, d.fmt == SVDQ_FMT_MX ? B * d.mx_scale_row_bytes() : 0);
+  sec(WS_DOWN, B * d.rp * (int64_t)dtype_size(d.dtype));
+  sec(WS_PARTIAL, p.k_chunks > 1 ? (int64_t)p.k_chunks * B * d.rp * 4 : 0);
+  sec(WS_AMAX, d.fmt == SVDQ_FMT_INT ? (int64_t)p.amax_blocks * 4 : 0);
+  sec(WS_SX, 16);
+  off[WS_END] = o;
+}
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SVDQ_OK;
+  return set_error(SVDQ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_linear_dims(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_format(fmt, bits))) return st;
+  if (B < 1 || M < 1 || N < 1) return set_error(SVDQ_EINVAL, "B, M and N must be >= 1");
+  if (B > kMaxDim || M > kMaxDim || N > kMaxDim) return set_error(SVDQ_EINVAL, "dimension too large");
+  if (rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "rank must be in [0, min(M, N)]");
+  return SVDQ_OK;
+}
+
+}  // namespace
+}  // namespace svdq
+
+using namespace svdq;
+
+extern "C" {
+
+int svdq_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
+                         size_t* bytes_out) {
+  clear_error();
+  int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
+  if (st) return st;
+  if (!bytes_out) return set_error(SVDQ_EINVAL, "bytes_out is NULL");
+  const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
+  int64_t off[WS_NSEC];
+  workspace_layout(d, make_plan(d, B), off);
+  *bytes_out = (size_t)off[WS_END];
+  return SVDQ_OK;
+}
+
+int svdq_smooth_inputs(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t sxm, const void* weight, int64_t N,
+                       int64_t swm, int64_t swn, const float* scale, int dtype, void* xs_out, int64_t ldxs,
+                       void* ws_out, int64_t ldws, svdq_stream_t stream) {
+  clear_error();
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (!scale) return set_error(SVDQ_EINVAL, "scale is NULL");
+  if (M < 1 || M > kMaxDim) return set_error(SVDQ_EINVAL, "M must be >= 1");
+  const bool do_x = x && xs_out, do_w = weight && ws_out;
+  if (!do_x && !do_w) return set_error(SVDQ_EINVAL, "nothing to smooth");
+  if (do_x && (B < 1 || B > kMaxDim || ldxs < M)) return set_error(SVDQ_EINVAL, "bad x shape or xs row stride");
+  if (do_w && (N < 1 || N > kMaxDim || ldws < N)) return set_error(SVDQ_EINVAL, "bad weight shape or ws row stride");
+  return hip_status(launch_smooth(do_x ? x : nullptr, B, M, sxb, sxm, do_w ? weight : nullptr, N, swm, swn, scale,
+                                  dtype, do_x ? xs_out : nullptr, ldxs, do_w ? ws_out : nullptr, ldws,
+                                  (hipStream_t)stream),
+                    "smooth_inputs launch");
+}
+
+size_t svdq_fake_quantize_workspace(int64_t rows, int64_t cols) {
+  (void)cols;
+  const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(rows, 1024));
+  return (size_t)round_up(parts * 4, kAlign);
+}
+
+int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, int dtype, int bits,
+                       void* out, int64_t ldo, float* s_out, void* workspace, size_t workspace_bytes,
+                       svdq_stream_t stream) {
+  clear_error();
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_format(SVDQ_FMT_INT, bits))) return st;
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return set_error(SVDQ_EINVAL, "empty or too large tensor");
+  if (!z || !out || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
+  if (ldo < cols) return set_error(SVDQ_EINVAL, "output row stride smaller than cols");
+  if (workspace_bytes < svdq_fake_quantize_workspace(rows, cols)) return set_error(SVDQ_EINVAL, "workspace too small");
+  if (!aligned(workspace, 4)) return set_error(SVDQ_EINVAL, "workspace misaligned");
+  const int parts = (int)std::min<int64_t>(rows, 1024);
+  hipStream_t s = (hipStream_t)stream;
+  float* part = (float*)workspace;
+  if ((st = hip_status(launch_amax(z, rows, cols, szr, szc, nullptr, dtype, part, parts, s), "fake_quantize max"))) return st;
+  return hip_status(launch_fake_quant(z, rows, cols, szr, szc, dtype, bits, part, parts, out, ldo, s_out, s),
+                    "fake_quantize launch");
+}
+
+int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, const float* scale, int fmt, int bits,
+                              int dtype, void* codes_out, int64_t ldc, void* scales_out, int64_t lds, float* sx_out,
+                              void* workspace, size_t workspace_bytes, svdq_stream_t stream) {
+  clear_error();
+  int st = check_linear_dims(B, M, 1, 0, fmt, bits, dtype);
+  if (st) return st;
+  if (!x || !scale || !codes_out || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
+  if (fmt == SVDQ_FMT_MX && !scales_out) return set_error(SVDQ_EINVAL, "MX needs scales_out");
+  const Dims d = make_dims(M, 1, 0, fmt, bits, dtype);
+  if (ldx < M) return set_error(SVDQ_EINVAL, "x row stride smaller than M");
+  if (ldc < d.code_row_bytes() || ldc % 16 || !aligned(codes_out, 16))
+    return set_error(SVDQ_EINVAL, "codes_out must be 16-byte aligned with a row stride >= the padded width and a multiple of 16");
+  if (fmt == SVDQ_FMT_MX && lds < d.mx_scale_row_bytes()) return set_error(SVDQ_EINVAL, "scale row stride too small");
+  if (!aligned(scale, 16)) return set_error(SVDQ_EINVAL, "scale must be 16-byte aligned");
+  const LaunchPlan pl = make_plan(d, B);
+  int64_t off[WS_NSEC];
+  workspace_layout(d, pl, off);
+  if (workspace_bytes < (size_t)off[WS_END] || !aligned(workspace, kAlign))
+    return set_error(SVDQ_EINVAL, "workspace too small or not 256-byte aligned");
+  uint8_t* ws = (uint8_t*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  float* amax = (float*)(ws + off[WS_AMAX]);
+  if (fmt == SVDQ_FMT_INT) {
+    if ((st = hip_status(launch_amax(x, B, M, ldx, 1, scale, dtype, amax, pl.amax_blocks, s), "activation max")))
+      return st;
+  }
+  ActParams p{};
+  p.x = x;
+  p.ldx = ldx;
+  p.B = (int)B;
+  p.M = (int)M;
+  p.Kp = (int)d.Kp;
+  p.scale = scale;
+  p.codes = (uint8_t*)codes_out;
+  p.ldc = ldc;
+  p.mxs = (uint8_t*)scales_out;
+  p.lds = lds;
+  p.amax_part = amax;
+  p.n_amax = pl.amax_blocks;
+  p.bits = bits;
+  p.sx_out = sx_out;
+  p.l1t = nullptr;
+  p.rp = 0;
+  p.k_chunks = pl.k_chunks;
+  p.k_chunk_len = pl.k_chunk_len;
+  p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
+  return hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, 1, s), "quantize_activations launch");
+}
+
+int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob, int64_t N, int64_t rank, int fmt,
+                int bits, int dtype, void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                svdq_stream_t stream) {
+  clear_error();
+  int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
+  if (st) return st;
+  if (!x || !blob || !y || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
+  if (ldx < M) return set_error(SVDQ_EINVAL, "x row stride smaller than M");
+  if (ldy < N) return set_error(SVDQ_EINVAL, "y row stride smaller than N");
+  if (!aligned(blob, kAlign)) return set_error(SVDQ_EINVAL, "prepared blob must be 256-byte aligned");
+  if (!aligned(y, dtype_size(dtype)) || !aligned(x, dtype_size(dtype))) return set_error(SVDQ_EINVAL, "x or y misaligned");
+  const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
+  const LaunchPlan pl = make_plan(d, B);
+  int64_t woff[WS_NSEC], boff[SVDQ_NSEC];
+  workspace_layout(d, pl, woff);
+  blob_layout(d, boff);
+  if (workspace_bytes < (size_t)woff[WS_END] || !aligned(workspace, kAlign))
+    return set_error(SVDQ_EINVAL, "workspace too small or not 256-byte aligned");
+  const uint8_t* bl = (const uint8_t*)blob;
+  uint8_t* ws = (uint8_t*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  float* amax = (float*)(ws + woff[WS_AMAX]);
+  float* sx = (float*)(ws + woff[WS_SX]);
+  const float* scale = (const float*)(bl + boff[SVDQ_SEC_SCALE]);
+
+  // (a) + (b): smooth, quantise, down-project
+  if (fmt == SVDQ_FMT_INT) {
+    if ((st = hip_status(launch_amax(x, B, M, ldx, 1, scale, dtype, amax, pl.amax_blocks, s), "activation max")))
+      return st;
+  }
+  ActParams p{};
+  p.x = x;
+  p.ldx = ldx;
+  p.B = (int)B;
+  p.M = (int)M;
+  p.Kp = (int)d.Kp;
+  p.scale = scale;
+  p.codes = ws + woff[WS_CODES];
+  p.ldc = d.code_row_bytes();
+  p.mxs = ws + woff[WS_SCALES];
+  p.lds = d.mx_scale_row_bytes();
+  p.amax_part = amax;
+  p.n_amax = pl.amax_blocks;
+  p.bits = bits;
+  p.sx_out = sx;
+  p.l1t = bl + boff[SVDQ_SEC_L1T];
+  p.rp = (int)d.rp;
+  p.down_part = (float*)(ws + woff[WS_PARTIAL]);
+  p.down = ws + woff[WS_DOWN];
+  p.k_chunks = pl.k_chunks;
+  p.k_chunk_len = pl.k_chunk_len;
+  p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
+  const int r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 128) : 1;
+  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, r_chunks, s), "activation quantise launch")))
+    return st;
+  if (d.rp > 0 && pl.k_chunks > 1) {
+    if ((st = hip_status(launch_down_reduce(p.down_part, pl.k_chunks, (int)B, (int)d.rp, p.down, dtype, s),
+                         "down-projection reduce launch")))
+      return st;
+  }
+  // (c): residual GEMM + epilogue
+  GemmParams g{};
+  g.acodes = ws + woff[WS_CODES];
+  g.lda = d.code_row_bytes();
+  g.ascales = ws + woff[WS_SCALES];
+  g.ldas = d.mx_scale_row_bytes();
+  g.wcodes = bl + boff[SVDQ_SEC_RCODES];
+  g.ldw = d.code_row_bytes();
+  g.wscales = bl + boff[SVDQ_SEC_RSCALES];
+  g.ldws = d.mx_scale_row_bytes();
+  g.sx = sx;
+  g.sr = (const float*)(bl + boff[SVDQ_SEC_RSCALES]);
+  g.down = ws + woff[WS_DOWN];
+  g.l2t = bl + boff[SVDQ_SEC_L2T];
+  g.rp = (int)d.rp;
+  g.y = y;
+  g.ldy = ldy;
+  g.B = (int)B;
+  g.N = (int)N;
+  g.kstages = (int)(d.code_row_bytes() / 128);
+  return hip_status(launch_gemm(g, fmt, bits, dtype, s), "residual GEMM launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers of libsvdq (gfx950): storage types, the smoothing division, the
+// per-tensor INT and per-block MXFP4 quantisers, nibble unpacking and MFMA vector types.
+//
+// Quantisation follows "SVDQuant Smoothing, Low-rank and Residual Quantization"
+// ("Formula and conventions" items 1 and 3: xs = x / scale; s = max|z| / qmax,
+// codes = clamp(round half to even(z / s))) and the MXFP4 per-block minmax scheme of the
+// msModelSlim SVDQuant guide (step 2). Every value that decides a code is a single IEEE
+// binary32 operation (division, bf16 rounding, power-of-two scaling), never a reciprocal
+// multiply or a contracted FMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+namespace dev {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32;
+typedef uint64_t u64;
+
+// ---- storage dtypes ---------------------------------------------------------------------
+struct F32 {
+  typedef float T;
+  static constexpr bool is_bf16 = false;
+  __device__ static inline float to_f32(T v) { return v; }
+  __device__ static inline T from_f32(float v) { return v; }
+};
+struct BF16 {
+  typedef uint16_t T;  // raw bfloat16 bits
+  static constexpr bool is_bf16 = true;
+  __device__ static inline float to_f32(T v) { return __uint_as_float((u32)v << 16); }
+  // round to nearest, ties to even (inputs are finite)
+  __device__ static inline T from_f32(float v) {
+    u32 u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (T)(u >> 16);
+  }
+};
+
+// D(x / s): one IEEE binary32 division, then rounding to the storage dtype.
+template <class DT>
+__device__ inline float smooth_value(float x, float s) {
+  return DT::to_f32(DT::from_f32(x / s));
+}
+
+// ---- MXFP4 ------------------------------------------------------------------------------
+// Shared exponent of a 32-element block from its max magnitude a: the smallest e with
+// a <= 6 * 2^e, clamped to [-127, 127] (E8M0 byte = e + 127). For normal a = 1.m * 2^E the
+// answer is E - 2, or E - 1 when 1.m > 1.5; a below 2^-126 (including 0) gives -127.
+__device__ inline int mx_exponent(float a) {
+  const u32 u = __float_as_uint(a);
+  const int be = (int)(u >> 23);
+  if (be == 0) return -127;
+  const int e = be - 129 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^e as a float for e in [-127, 127] (2^-127 is subnormal).
+__device__ inline float pow2f(int e) {
+  return e >= -126 ? __uint_as_float((u32)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+// Eight E2M1 codes of v[0..7] / 2^e packed into one word (element 2p in the low nibble of
+// byte p). v_cvt_scalef32_pk_fp4_f32 divides by the power-of-two scale and rounds to the
+// nearest E2M1 value, ties to the even code, keeping the sign of zero.
+__device__ inline u32 fp4_pack8(const float* v, float scale) {
+  u32 r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+  return r;
+}
+
+// ---- per-tensor INT ---------------------------------------------------------------------
+// clamp(round_half_even(z / s), -qmax, qmax) with an IEEE division; s == 0 gives code 0.
+__device__ inline int int_code(float z, float s, float qmax) {
+  if (s == 0.f) return 0;
+  const float r = __builtin_rintf(z / s);
+  return (int)fminf(fmaxf(r, -qmax), qmax);
+}
+
+// Sign-extend eight 4-bit two's-complement codes (one word, code j in nibble j) into two
+// words of int8 lanes: lo = codes 0,2,4,6 and hi = codes 1,3,5,7. The order inside a lane
+// is irrelevant to the matrix cores as long as both operands use it.
+__device__ inline void unpack_nibbles(u32 w, u32& lo, u32& hi) {
+  const u32 e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+  // per byte t in [0,15]: ((t ^ 8) | 0x80) - 8 never borrows; ^ 0x80 yields int8(t - 16*(t>=8))
+  lo = (((e ^ 0x08080808u) | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+  hi = (((o ^ 0x08080808u) | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+}
+
+// ---- wave / block reductions ------------------------------------------------------------
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace dev
+}  // namespace svdq

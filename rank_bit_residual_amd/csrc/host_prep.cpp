@@ -1,0 +1,312 @@
+// Host side of libsvdq: argument checks, dtype conversion, the one-time weight preparation
+// (fold the smoothing scale into W, truncated SVD split, residual, residual quantisation and
+// packing into the prepared blob) and the host-only C ABI calls.
+//
+// Page references (title, section):
+//   "SVDQuant Smoothing, Low-rank and Residual Quantization" — "Functions / Return
+//     requirements" (_check_smoothing, _check_rank, split_weight) and "Formula and
+//     conventions" items 1-3 (ws = scale[:,None] * W; truncated SVD; quantise R, not ws;
+//     per-tensor INT with ties to even).
+//   "SVDQuant 参数配置流程指南" (msModelSlim), step 2: MXFP4 per_block minmax weights.
+//   "flashinfer.gemm.svdquant_linear": invariant per-layer transforms prepared offline,
+//     rank a multiple of 32 (we zero-pad instead), residual codes stored per output column
+//     with K contiguous.
+//
+// Built without FP contraction: every quantity that decides a code is one IEEE binary32
+// operation, as in the definition.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "host_svd.h"
+#include "svdq_internal.h"
+
+namespace svdq {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int set_error(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+void clear_error() { g_last_error.clear(); }
+
+int check_dtype(int dtype) {
+  if (dtype == SVDQ_F32 || dtype == SVDQ_BF16) return SVDQ_OK;
+  if (dtype == SVDQ_F64) return set_error(SVDQ_EDTYPE, "float64 is not supported by the device library");
+  return set_error(SVDQ_EDTYPE, "unknown dtype code " + std::to_string(dtype));
+}
+
+int check_format(int fmt, int bits) {
+  if (fmt == SVDQ_FMT_INT) {
+    if (bits < 2 || bits > 8) return set_error(SVDQ_EINVAL, "bits must be in [2, 8]");
+    return SVDQ_OK;
+  }
+  if (fmt == SVDQ_FMT_MX) {
+    if (bits != 4) return set_error(SVDQ_EINVAL, "MXFP4 uses 4-bit codes (bits must be 4)");
+    return SVDQ_OK;
+  }
+  return set_error(SVDQ_EINVAL, "unknown format code " + std::to_string(fmt));
+}
+
+void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]) {
+  int64_t o = 0;
+  auto sec = [&](int id, int64_t bytes) {
+    off[id] = o;
+    o = round_up(o + bytes, kAlign);
+  };
+  sec(SVDQ_SEC_SCALE, d.M * 4);
+  sec(SVDQ_SEC_RCODES, d.Np * d.code_row_bytes());
+  sec(SVDQ_SEC_RSCALES, d.fmt == SVDQ_FMT_MX ? d.Np * d.mx_scale_row_bytes() : 16);
+  sec(SVDQ_SEC_L1T, d.rp * d.Kp * (int64_t)dtype_size(d.dtype));
+  sec(SVDQ_SEC_L2T, d.Np * d.rp * (int64_t)dtype_size(d.dtype));
+  off[SVDQ_SEC_END] = o;
+}
+
+namespace {
+
+// ---- dtype conversion (finite values) --------------------------------------------------
+inline float bf16_bits_to_float(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+inline uint16_t float_to_bf16_bits(float f) {  // round to nearest, ties to even
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// double -> bf16 with a single rounding: scale by the spacing of bf16 numbers around v.
+inline uint16_t double_to_bf16_bits(double v) {
+  if (v == 0.0) return std::signbit(v) ? 0x8000 : 0;
+  const int e = std::max(std::ilogb(v), -126);
+  const double q = std::ldexp(1.0, e - 7);
+  const float r = (float)(std::nearbyint(v / q) * q);  // exact: <= 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &r, 4);
+  return (uint16_t)(u >> 16);
+}
+
+struct HostMat {  // read-only view of a dtype matrix on the host
+  const void* p;
+  int64_t ld;
+  int dtype;
+  float at(int64_t i, int64_t j) const {
+    if (dtype == SVDQ_F32) return ((const float*)p)[i * ld + j];
+    return bf16_bits_to_float(((const uint16_t*)p)[i * ld + j]);
+  }
+};
+
+// Store a float that is already representable in dtype.
+inline void store_exact(void* base, int64_t idx, int dtype, float v) {
+  if (dtype == SVDQ_F32)
+    ((float*)base)[idx] = v;
+  else
+    ((uint16_t*)base)[idx] = float_to_bf16_bits(v);
+}
+// Round a binary32 result to dtype (RNE for bf16).
+inline float round_f32(float v, int dtype) { return dtype == SVDQ_F32 ? v : bf16_bits_to_float(float_to_bf16_bits(v)); }
+// Round a float64 result to dtype with one rounding.
+inline float round_f64(double v, int dtype) {
+  return dtype == SVDQ_F32 ? (float)v : bf16_bits_to_float(double_to_bf16_bits(v));
+}
+
+// ---- quantisers ------------------------------------------------------------------------
+// MXFP4 shared exponent: smallest e with a <= 6 * 2^e (clamped to [-127, 127]).
+// For normal a = 1.m * 2^E: e = E - 2 when 1.m <= 1.5, else E - 1; a < 2^-126 gives -127.
+inline int mx_exponent(float a) {
+  uint32_t u;
+  std::memcpy(&u, &a, 4);
+  const int be = (int)((u >> 23) & 0xFF);
+  const uint32_t mant = u & 0x7FFFFFu;
+  if (be == 0) return -127;
+  const int e = (be - 127) - 2 + (mant > 0x400000u ? 1 : 0);
+  return std::min(127, std::max(-127, e));
+}
+// E2M1 code of z / 2^e: magnitude thresholds are the midpoints of {0,.5,1,1.5,2,3,4,6};
+// at a midpoint the even code wins (0.25->0, 0.75->2, 1.25->2, 1.75->4, 2.5->4, 3.5->6, 5->6).
+inline uint8_t e2m1_code(float z, int e) {
+  const float v = std::ldexp(std::fabs(z), -e);
+  const int c = (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) + (v >= 3.5f) + (v > 5.0f);
+  return (uint8_t)(c | (std::signbit(z) ? 8 : 0));
+}
+
+int validate_prepare(int64_t M, int64_t N, int64_t ldw, int64_t rank, int fmt, int bits, int dtype) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_format(fmt, bits))) return st;
+  if (M < 1 || N < 1) return set_error(SVDQ_EINVAL, "weight must be a nonempty matrix");
+  if (ldw < N) return set_error(SVDQ_EINVAL, "weight row stride smaller than N");
+  if (rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "rank must be in [0, min(M, N)]");
+  return SVDQ_OK;
+}
+
+// Split ws [M,N] (float values exact in dtype) into rounded factors and the residual.
+void split(const std::vector<float>& ws, int64_t M, int64_t N, int64_t rank, int dtype, std::vector<float>& L1,
+           std::vector<float>& L2, std::vector<float>& R) {
+  L1.assign((size_t)(M * rank), 0.f);
+  L2.assign((size_t)(rank * N), 0.f);
+  R.assign((size_t)(M * N), 0.f);
+  if (rank == 0) {
+    R = ws;
+    return;
+  }
+  std::vector<double> l1((size_t)(M * rank)), l2((size_t)(rank * N));
+  host::truncated_svd(ws.data(), M, N, N, rank, l1.data(), l2.data());
+  for (size_t i = 0; i < l1.size(); i++) L1[i] = round_f64(l1[i], dtype);
+  for (size_t i = 0; i < l2.size(); i++) L2[i] = round_f64(l2[i], dtype);
+  // R = D(ws - L1 L2), the product in float64 from the stored factors
+  std::vector<double> prod((size_t)(M * N));
+  host::gemm<float, float>(M, N, rank, L1.data(), rank, 1, L2.data(), N, 1, prod.data(), N);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M * N; i++) R[i] = round_f64((double)ws[i] - prod[i], dtype);
+}
+
+}  // namespace
+}  // namespace svdq
+
+using namespace svdq;
+
+extern "C" {
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+const char* svdq_version(void) { return "svdq 0.1 gfx950"; }
+
+int svdq_check_smoothing(int64_t B, int64_t M, int64_t Mw, int64_t Ms, int64_t N, const float* scale_host) {
+  clear_error();
+  if (B < 1 || M < 1 || N < 1 || Mw < 1 || Ms < 1) return set_error(SVDQ_EINVAL, "x, weight and scale must be nonempty");
+  if (M != Mw || M != Ms) return set_error(SVDQ_EINVAL, "input-channel sizes of x, weight and scale differ");
+  if (!scale_host) return set_error(SVDQ_EINVAL, "scale is NULL");
+  for (int64_t m = 0; m < M; m++) {
+    const float s = scale_host[m];
+    if (!(std::isfinite(s) && s > 0.f))
+      return set_error(SVDQ_EINVAL, "scale must be positive and finite (index " + std::to_string(m) + ")");
+  }
+  return SVDQ_OK;
+}
+
+int svdq_check_rank(int64_t M, int64_t N, int64_t rank) {
+  clear_error();
+  if (M < 1 || N < 1) return set_error(SVDQ_EINVAL, "weight must be a nonempty matrix");
+  if (rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "rank must be in [0, min(M, N)]");
+  return SVDQ_OK;
+}
+
+int svdq_split_weight(const void* weight, int64_t M, int64_t N, int64_t ldw, int dtype, int64_t rank, void* left,
+                      void* right, void* residual) {
+  clear_error();
+  int st = validate_prepare(M, N, ldw, rank, SVDQ_FMT_INT, 4, dtype);
+  if (st) return st;
+  if (!weight || !residual || (rank > 0 && (!left || !right)))
+    return set_error(SVDQ_EINVAL, "NULL buffer passed to split_weight");
+  HostMat W{weight, ldw, dtype};
+  std::vector<float> ws((size_t)(M * N));
+  for (int64_t i = 0; i < M; i++)
+    for (int64_t j = 0; j < N; j++) ws[i * N + j] = W.at(i, j);
+  std::vector<float> L1, L2, R;
+  split(ws, M, N, rank, dtype, L1, L2, R);
+  for (int64_t i = 0; i < M * rank; i++) store_exact(left, i, dtype, L1[i]);
+  for (int64_t i = 0; i < rank * N; i++) store_exact(right, i, dtype, L2[i]);
+  for (int64_t i = 0; i < M * N; i++) store_exact(residual, i, dtype, R[i]);
+  return SVDQ_OK;
+}
+
+int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype, int64_t offsets[SVDQ_NSEC]) {
+  clear_error();
+  int st = validate_prepare(M, N, N, rank, fmt, bits, dtype);
+  if (st) return st;
+  blob_layout(make_dims(M, N, rank, fmt, bits, dtype), offsets);
+  return SVDQ_OK;
+}
+
+int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale, int64_t rank, int fmt,
+                 int bits, int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out) {
+  clear_error();
+  int st = validate_prepare(M, N, ldw, rank, fmt, bits, dtype);
+  if (st) return st;
+  if (!weight || !scale || !blob_host) return set_error(SVDQ_EINVAL, "NULL buffer passed to prepare");
+  if ((st = svdq_check_smoothing(1, M, M, M, N, scale))) return st;
+  const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
+  int64_t off[SVDQ_NSEC];
+  blob_layout(d, off);
+  uint8_t* blob = (uint8_t*)blob_host;
+  std::memset(blob, 0, (size_t)off[SVDQ_SEC_END]);
+
+  // fold: ws = D(scale[m] * W[m,n]), one binary32 multiply and one rounding
+  HostMat W{weight, ldw, dtype};
+  std::vector<float> ws((size_t)(M * N));
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; i++)
+    for (int64_t j = 0; j < N; j++) ws[i * N + j] = round_f32(scale[i] * W.at(i, j), dtype);
+
+  std::vector<float> L1, L2, R;
+  split(ws, M, N, rank, dtype, L1, L2, R);
+
+  std::memcpy(blob + off[SVDQ_SEC_SCALE], scale, (size_t)M * 4);
+
+  uint8_t* codes = blob + off[SVDQ_SEC_RCODES];
+  const int64_t crow = d.code_row_bytes();
+  if (fmt == SVDQ_FMT_INT) {
+    // one scale for the whole residual: s = max|R| / qmax, codes = clamp(rint(R / s))
+    const int qmax = (1 << (bits - 1)) - 1;
+    float a = 0.f;
+    for (float v : R) a = std::max(a, std::fabs(v));
+    const float s = a / (float)qmax;
+    std::memcpy(blob + off[SVDQ_SEC_RSCALES], &s, 4);
+    if (a > 0.f) {
+#pragma omp parallel for schedule(static)
+      for (int64_t n = 0; n < N; n++) {
+        for (int64_t m = 0; m < M; m++) {
+          const float q = R[m * N + n] / s;
+          const int c = (int)std::max<float>(-(float)qmax, std::min<float>((float)qmax, std::nearbyint(q)));
+          if (d.nibbles())
+            codes[n * crow + m / 2] |= (uint8_t)((c & 0xF) << (4 * (m & 1)));
+          else
+            codes[n * crow + m] = (uint8_t)(int8_t)c;
+        }
+      }
+    }
+  } else {
+    // MXFP4 per column n of R, 32-element blocks along m
+    uint8_t* sc = blob + off[SVDQ_SEC_RSCALES];
+    const int64_t srow = d.mx_scale_row_bytes();
+    const int64_t nb = ceil_div(M, kMxBlock);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+      for (int64_t b = 0; b < nb; b++) {
+        const int64_t m0 = b * kMxBlock, m1 = std::min(M, m0 + kMxBlock);
+        float a = 0.f;
+        for (int64_t m = m0; m < m1; m++) a = std::max(a, std::fabs(R[m * N + n]));
+        const int e = mx_exponent(a);
+        sc[n * srow + b] = (uint8_t)(e + 127);
+        for (int64_t m = m0; m < m1; m++)
+          codes[n * crow + m / 2] |= (uint8_t)(e2m1_code(R[m * N + n], e) << (4 * (m & 1)));
+      }
+    }
+  }
+  // low-rank factors, transposed and zero-padded: L1^T [rp, Kp], L2^T [Np, rp]
+  void* l1t = blob + off[SVDQ_SEC_L1T];
+  void* l2t = blob + off[SVDQ_SEC_L2T];
+  for (int64_t t = 0; t < rank; t++)
+    for (int64_t m = 0; m < M; m++) store_exact(l1t, t * d.Kp + m, dtype, L1[m * rank + t]);
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t t = 0; t < rank; t++) store_exact(l2t, n * d.rp + t, dtype, L2[t * N + n]);
+
+  if (left_out)
+    for (int64_t i = 0; i < M * rank; i++) store_exact(left_out, i, dtype, L1[i]);
+  if (right_out)
+    for (int64_t i = 0; i < rank * N; i++) store_exact(right_out, i, dtype, L2[i]);
+  if (residual_out)
+    for (int64_t i = 0; i < M * N; i++) store_exact(residual_out, i, dtype, R[i]);
+  return SVDQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel launchers of libsvdq (device code in k_act.hip / k_gemm.hip, called from capi.hip).
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+struct ActParams {
+  const void* x;
+  int64_t ldx;
+  int B, M, Kp;
+  const float* scale;
+  uint8_t* codes;  // [B][ldc] bytes, or NULL (down-projection only)
+  int64_t ldc;
+  uint8_t* mxs;  // MX scales [B][lds]
+  int64_t lds;
+  const float* amax_part;  // INT: per-block maxima of |X^|
+  int n_amax;
+  int bits;
+  float* sx_out;  // INT: receives s_x (may be NULL)
+  const void* l1t;  // [rp][Kp] dtype
+  int rp;
+  float* down_part;  // [k_chunks][B][rp] f32 when k_chunks > 1
+  void* down;        // [B][rp] dtype when k_chunks == 1
+  int k_chunks, k_chunk_len;
+  int x_vec_ok;  // x base and row stride allow 16-byte loads
+};
+
+struct GemmParams {
+  const uint8_t* acodes;
+  int64_t lda;
+  const uint8_t* ascales;
+  int64_t ldas;
+  const uint8_t* wcodes;
+  int64_t ldw;
+  const uint8_t* wscales;
+  int64_t ldws;
+  const float* sx;
+  const float* sr;
+  const void* down;
+  const void* l2t;
+  int rp;
+  void* y;
+  int64_t ldy;
+  int B, N, kstages;
+};
+
+hipError_t launch_smooth(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t sxm, const void* w, int64_t N,
+                         int64_t swm, int64_t swn, const float* scale, int dtype, void* xs, int64_t ldxs, void* ws,
+                         int64_t ldws, hipStream_t stream);
+// Per-block maxima of |z| (smoothed by `scale` when non-NULL) into part[nparts].
+hipError_t launch_amax(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, const float* scale,
+                       int dtype, float* part, int nparts, hipStream_t stream);
+hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, int dtype, int bits,
+                             const float* part, int nparts, void* out, int64_t ldo, float* s_out, hipStream_t stream);
+hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream);
+hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, void* down, int dtype,
+                              hipStream_t stream);
+hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
+
+}  // namespace svdq

@@ -15,3 +15,8 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # name the case on its own flushed line before it runs, so a crash still identifies it
+    print(f"\n[start] {nodeid}", flush=True)

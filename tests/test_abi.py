@@ -1,0 +1,49 @@
+"""The C ABI library loads without a GPU and exports every function include/svdq.h declares."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_bit_residual_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "svdq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_page_calls():
+    names = declared_functions()
+    for required in ("svdq_smooth_inputs", "svdq_split_weight", "svdq_fake_quantize", "svdq_linear"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    assert set(declared_functions()) <= set(_lib.SIGNATURES)
+
+
+def test_host_calls_report_errors_without_a_gpu():
+    lib = _lib.load()
+    assert lib.svdq_check_rank(4, 3, 4) == _lib.SVDQ_EINVAL
+    assert b"rank" in lib.svdq_last_error()
+    assert lib.svdq_check_rank(4, 3, 3) == _lib.SVDQ_OK
+    assert lib.svdq_last_error() == b""
+    off = (ctypes.c_int64 * 6)()
+    assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_MX, 3, _lib.SVDQ_BF16, off) == _lib.SVDQ_EINVAL
+    assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F64, off) == _lib.SVDQ_EDTYPE
+    assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_INT, 9, _lib.SVDQ_F32, off) == _lib.SVDQ_EINVAL
+    assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F32, off) == _lib.SVDQ_OK
+    assert all(v % 256 == 0 for v in off)
+    ws = ctypes.c_size_t()
+    assert lib.svdq_workspace_bytes(16, 64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F32, ctypes.byref(ws)) == 0
+    assert ws.value > 0

@@ -1,0 +1,217 @@
+"""GPU parity of libsvdq against the CPU oracle (runs through the C ABI on an MI355X).
+
+Integer and byte outputs (activation codes, E8M0 scales, s_x, smoothing results,
+fake-quantised values) must match the oracle bit for bit. The operator output Y must be
+within a relative Frobenius error of 2e-3 (float32 inputs) or 1e-2 (bfloat16 inputs) of
+the oracle's float64 forward on the library's own exported factors and residual; exact
+special cases (rank 0, unit scale, values the quantiser reproduces exactly) must match
+x @ W bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rank_bit_residual_amd as R
+from oracle import svdquant as O
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 2e-3, "bf16": 1e-2}
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _g(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(TD[dtype]).to(dev())
+
+
+def _np(t):
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+# ----------------------------------------------------------------------------- elementwise calls
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_smooth_inputs_bit_exact(dtype):
+    rng = np.random.default_rng(10)
+    x = O.to_dtype(rng.standard_t(3, (37, 300)) * 10.0 ** rng.integers(-3, 4, (37, 300)), dtype)
+    w = O.to_dtype(rng.standard_normal((300, 70)), dtype)
+    s = np.abs(rng.standard_normal(300)).astype(np.float32) * np.float32(3) + np.float32(1e-3)
+    x[0, :5] = [0.0, -0.0, 1e-38, -3e-39, 65504.0]
+    xs, ws = R.smooth_inputs(_g(x, dtype), _g(w, dtype), torch.from_numpy(s).to(dev()))
+    oxs, ows = O.smooth_inputs(x, w, s, dtype)
+    assert np.array_equal(_bits(_np(xs)), _bits(oxs)) and np.array_equal(_bits(_np(ws)), _bits(ows))
+    # strided (transposed) inputs
+    xt = _g(x.T.copy(), dtype).t()
+    xs2, _ = R.smooth_inputs(xt, _g(w, dtype), torch.from_numpy(s).to(dev()))
+    assert torch.equal(xs2, xs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+def test_fake_quantize_bit_exact(dtype, bits):
+    rng = np.random.default_rng(bits)
+    z = O.to_dtype(rng.standard_normal((129, 77)) * 3, dtype)
+    got = R.fake_quantize(_g(z, dtype), bits)
+    assert got.dtype == TD[dtype] and got.shape == (129, 77)
+    assert np.array_equal(_bits(_np(got)), _bits(O.fake_quantize(z, bits, dtype)))
+
+
+def test_fake_quantize_zero_and_worked_ties():
+    z = torch.zeros(5, 9, device=dev())
+    assert not R.fake_quantize(z, 4).any()
+    t = torch.tensor([[7, 3.5, 2.5, -0.5, -1.5, 0]], device=dev())
+    assert R.fake_quantize(t, 4).tolist() == [[7, 4, 2, 0, -2, 0]]
+    t = torch.tensor([[105, 37.5]], device=dev())
+    assert R.fake_quantize(t, 4).tolist() == [[105, 30]]
+
+
+# ----------------------------------------------------------------------------- step (a): codes
+def _act_codes_ref(x, s, fmt, bits, dtype):
+    xs = O.smooth_activations(x, s, dtype)
+    if fmt == "mx":
+        c, sb = O.quantize_mx(xs)
+        return O.pack_nibbles(c), sb, None
+    c, sx = O.quantize_int(xs, bits, dtype)
+    return O.pack_int_codes(c, bits), None, sx
+
+
+def _check_codes(x, s, fmt, bits, dtype):
+    codes, scales, sx = R.quantize_activations(_g(x, dtype), torch.from_numpy(s).to(dev()), fmt, bits)
+    torch.cuda.synchronize()
+    wc, ws, wsx = _act_codes_ref(x, s, fmt, bits, dtype)
+    codes = codes.cpu().numpy()
+    assert np.array_equal(codes[:, : wc.shape[1]], wc)
+    assert not codes[:, wc.shape[1]:].any()
+    if fmt == "mx":
+        sc = scales.cpu().numpy()
+        assert np.array_equal(sc[:, : ws.shape[1]], ws)
+    else:
+        assert sx.cpu().numpy()[0] == np.float32(wsx)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_activation_codes_bit_exact_workloads(cid):
+    wl = WORKLOADS[cid]
+    x, w, s = make_inputs(cid)
+    _check_codes(x, s, wl.fmt, wl.bits, wl.dtype)
+
+
+@pytest.mark.parametrize("fmt,bits,dtype", [("mx", 4, "bf16"), ("mx", 4, "f32"), ("int", 4, "bf16"), ("int", 3, "f32"),
+                                             ("int", 8, "bf16"), ("int", 6, "f32")])
+def test_activation_codes_edge_values(fmt, bits, dtype):
+    """Ragged K (M = 300: a short last block), ties, signed zeros, subnormals, huge values."""
+    rng = np.random.default_rng(11)
+    B, M = 19, 300
+    x = rng.standard_normal((B, M)) * 10.0 ** rng.integers(-2, 3, (B, M))
+    grid = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.0])
+    x[1] = grid[rng.integers(0, len(grid), M)]
+    x[2] = 0.0
+    x[3, :40] = -0.0
+    x[4] = rng.standard_normal(M) * 1e-39
+    x[5] = rng.standard_normal(M) * 1e30
+    x = O.to_dtype(x, dtype)
+    s = np.ones(M, np.float32)
+    s[100:] = np.abs(rng.standard_normal(M - 100)).astype(np.float32) + np.float32(0.01)
+    _check_codes(x, s, fmt, bits, dtype)
+
+
+# ----------------------------------------------------------------------------- exact special cases
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_int_exact_special_case(dtype):
+    """rank 0, unit scale, integer x and W with max |.| = 7: s_x = s_R = 1 and Y = x @ W exactly."""
+    rng = np.random.default_rng(12)
+    B, M, N = 40, 320, 300
+    x = rng.integers(-7, 8, (B, M)).astype(np.float32)
+    w = rng.integers(-7, 8, (M, N)).astype(np.float32)
+    x[0, 0] = w[0, 0] = 7
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, 4, "int")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x.astype(np.float64) @ w.astype(np.float64), dtype)
+    assert np.array_equal(_bits(_np(y)), _bits(want))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_exact_special_case(dtype):
+    """rank 0, unit scale, E2M1-grid values whose every 32-block (rows of x, columns of W)
+    has max 4 or 6: the shared exponent is 0, Q is the identity and Y = x @ W exactly."""
+    rng = np.random.default_rng(13)
+    B, M, N = 40, 320, 300
+    grid = O.E2M1_GRID
+    x = grid[rng.integers(0, 8, (B, M))] * np.where(rng.random((B, M)) < 0.5, -1, 1)
+    w = grid[rng.integers(0, 8, (M, N))] * np.where(rng.random((M, N)) < 0.5, -1, 1)
+    x[:, 0::32] = np.where(rng.random((B, M // 32)) < 0.5, 6.0, -4.0)
+    w[0::32, :] = np.where(rng.random((M // 32, N)) < 0.5, -6.0, 4.0)
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, 4, "mx")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x @ w, dtype)
+    assert np.array_equal(_bits(_np(y)), _bits(want))
+
+
+# ----------------------------------------------------------------------------- the operator
+def _parity(cid, B=None, rank=None, rows=None):
+    wl = WORKLOADS[cid]
+    rank = wl.rank if rank is None else rank
+    x, w, s = make_inputs(cid, B=B)
+    p = R.prepare(_g(w, wl.dtype), torch.from_numpy(s), rank, wl.bits, wl.fmt, keep_factors=True)
+    xg = _g(x, wl.dtype)
+    y = R.linear(xg, p)
+    y2 = R.linear(xg, p)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "repeated calls differ"
+    assert torch.equal(xg, _g(x, wl.dtype)), "input modified"
+    l, r, res = _np(p.left), _np(p.right), _np(p.residual)
+    if rows is not None:  # MXFP4 rows are independent: check a sample against the oracle
+        sel = np.random.default_rng(0).choice(x.shape[0], rows, replace=False)
+        ref = O.forward_ref(x[sel], s, l, r, res, wl.fmt, wl.bits, wl.dtype)
+        got = _np(y)[sel]
+    else:
+        ref = O.forward_ref(x, s, l, r, res, wl.fmt, wl.bits, wl.dtype)
+        got = _np(y)
+    err = O.rel_fro(got, ref)
+    print(f"workload {cid} B={x.shape[0]} rank={rank}: rel Frobenius error {err:.3e}")
+    assert err <= TOL[wl.dtype]
+    return err
+
+
+@pytest.mark.parametrize("cid", [1, 2, 5])
+def test_operator_parity_full_size(cid):
+    _parity(cid)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_operator_parity_full_size_sampled_rows(cid):
+    _parity(cid, rows=256)
+
+
+@pytest.mark.parametrize("cid,B", [(3, 77), (4, 130), (2, 33)])
+def test_operator_parity_ragged_batch(cid, B):
+    _parity(cid, B=B)
+
+
+@pytest.mark.parametrize("rank", [0, 1, 40, 48])
+def test_operator_parity_toy_ranks(rank):
+    _parity(1, rank=rank)
+
+
+def test_full_rank_recovers_product():
+    x, w, s = make_inputs(1)
+    y = R.svdquant_linear(_g(x, "f32"), _g(w, "f32"), torch.from_numpy(s).to(dev()), 48, 4)
+    assert O.rel_fro(_np(y), x.astype(np.float64) @ w.astype(np.float64)) <= 1e-4
+
+
+def test_strided_activations_match_contiguous():
+    x, w, s = make_inputs(3, B=64)
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(s), 32, 4, "mx")
+    big = torch.zeros(64, 3072 + 64, dtype=torch.bfloat16, device=dev())
+    big[:, 16:16 + 3072] = _g(x, "bf16")
+    assert torch.equal(R.linear(big[:, 16:16 + 3072], p), R.linear(_g(x, "bf16"), p))
