@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the SVDQuant linear operator on one MI355X.
+
+A step is one call of the whole per-call path (svdq_linear: smooth + quantise +
+down-projection, then the residual GEMM with the up-projection epilogue) over one batch
+of synthetic input already resident in HBM. Enough copies of (x, prepared weights, Y,
+workspace) rotate that no call is served from the 256 MB MALL.
+
+Prints one JSON line: value = 2*B*M*N*steps / wall time (TFLOP/s, eager launches),
+the roofline of the dominant kernel (the residual GEMM, timed with HIP events the library
+records around its own launches), and the CPU oracle's throughput on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+       python bench.py --pmc-summary FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "svdquant_linear TFLOP/s (2BMN) and % of MFMA/HBM roofline, 1×MI355X"
+# MI355X published dense peaks
+PEAK = {"hbm": 8000.0, "mxfp4": 10100.0, "int8": 5000.0, "bf16": 2500.0, "fp32": 157.3}
+GEMM_SRC = os.path.join(ROOT, "rank_bit_residual_amd", "csrc", "k_gemm.hip")
+
+
+def algorithmic(wl, B):
+    """Algorithmic work of one call and of one launch of the residual GEMM kernel."""
+    e = 2 if wl.dtype == "bf16" else 4
+    M, N, r = wl.M, wl.N, wl.rank
+    mx = wl.fmt == "mx"
+    code_bytes = (lambda rows, k: rows * k / 2) if (mx or wl.bits <= 4) else (lambda rows, k: rows * k)
+    r_scales = M * N / 32 if mx else 4
+    a_scales = B * M / 32 if mx else 4
+    call = B * M * e + 4 * M + B * N * e + code_bytes(N, M) + r_scales + (M + N) * r * e
+    gemm = code_bytes(B, M) + a_scales + code_bytes(N, M) + r_scales + B * r * e + N * r * e + B * N * e
+    return {"flops": 2.0 * B * M * N, "call_bytes": call, "gemm_bytes": gemm}
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic(workload_name):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"k_gemm_{workload_name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha") != source_sha(GEMM_SRC):
+        return None
+    return d.get("hbm_bytes_per_dispatch")
+
+
+def cpu_baseline(wl, x, s, prep, budget_s=10.0):
+    """The oracle's forward (numpy, float64 BLAS) on a row sample, repeated to ~budget_s."""
+    import torch
+    from oracle import svdquant as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"), default=0)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = 0
+    cores = cores or len(os.sched_getaffinity(0))
+    left = prep.left.to(torch.float32).numpy()
+    right = prep.right.to(torch.float32).numpy()
+    res = prep.residual.to(torch.float32).numpy()
+    rows = min(wl.B, 64)
+    t0 = time.perf_counter()
+    O.forward_ref(x[:rows], s, left, right, res, wl.fmt, wl.bits, wl.dtype)
+    one = time.perf_counter() - t0
+    # grow the sample (rows, then repetitions) towards the budget
+    if rows < wl.B and one < budget_s / 4:
+        rows = min(wl.B, int(rows * max(1.0, (budget_s / 4) / max(one, 1e-3))))
+    reps, done, t_total = 0, 0.0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        O.forward_ref(x[:rows], s, left, right, res, wl.fmt, wl.bits, wl.dtype)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        done += 2.0 * rows * wl.M * wl.N
+    return {"value": done / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle forward_ref on {rows} of {wl.B} rows x {reps} repetitions ({t_total:.1f} s), "
+                      f"float64 numpy BLAS on the host"}
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import rank_bit_residual_amd as R
+    from rank_bit_residual_amd import _lib as L
+    from workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x, w, s = make_inputs(wl)
+    prep = R.prepare(torch.from_numpy(w).to(td), torch.from_numpy(s), wl.rank, wl.bits, wl.fmt, device=dev,
+                     keep_factors=not args.no_cpu_baseline)
+    B, M, N = wl.B, wl.M, wl.N
+    wsb = R.workspace_bytes(B, prep)
+    x_g = torch.from_numpy(x).to(td).to(dev)
+    footprint = x_g.numel() * x_g.element_size() + prep.blob.numel() + B * N * x_g.element_size() + wsb
+    copies = max(2, math.ceil(args.rotate_mb * 2**20 / footprint))
+    xs = [x_g.clone() for _ in range(copies)]
+    blobs = [prep.blob.clone() for _ in range(copies)]
+    ys = [torch.empty((B, N), dtype=td, device=dev) for _ in range(copies)]
+    wss = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    lib = L.load()
+    stream = torch.cuda.current_stream(dev)
+    fmt = L.SVDQ_FMT_MX if wl.fmt == "mx" else L.SVDQ_FMT_INT
+    dt = L.SVDQ_BF16 if wl.dtype == "bf16" else L.SVDQ_F32
+    call_args = [(ctypes.c_void_p(xs[i].data_ptr()), B, M, M, ctypes.c_void_p(blobs[i].data_ptr()), N, wl.rank, fmt,
+                  wl.bits, dt, ctypes.c_void_p(ys[i].data_ptr()), N, ctypes.c_void_p(wss[i].data_ptr()), wsb,
+                  ctypes.c_void_p(stream.cuda_stream)) for i in range(copies)]
+    fn = lib.svdq_linear
+
+    def step(i):
+        st = fn(*call_args[i % copies])
+        if st:
+            L.check(st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: eager launches
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_eager = time.perf_counter() - t0
+    work = algorithmic(wl, B)
+    value = work["flops"] * args.steps / t_eager / 1e12
+
+    # ---- per-kernel HIP-event timing (events recorded by the library around each launch)
+    L.check(lib.svdq_profile_begin(args.steps))
+    for i in range(args.steps):
+        step(i)
+    ms = (ctypes.c_float * (args.steps * L.NSTAGES))()
+    n = ctypes.c_int()
+    L.check(lib.svdq_profile_end(ms, args.steps, ctypes.byref(n)))
+    per = np.array(ms[: n.value * L.NSTAGES], dtype=np.float64).reshape(n.value, L.NSTAGES)
+    stage_ms = {name: float(per[:, k].mean()) for k, name in enumerate(L.STAGE_NAMES) if per[:, k].any()}
+
+    # ---- HIP-graph replay of the same calls (reported separately, not the headline)
+    graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        per_graph = min(copies * 4, 64)
+        cap_stream = torch.cuda.Stream(dev)
+        cap_stream.wait_stream(stream)
+        with torch.cuda.stream(cap_stream):
+            gargs = [(a[:-1] + (ctypes.c_void_p(cap_stream.cuda_stream),)) for a in call_args]
+            for i in range(copies):  # warm the capture stream
+                L.check(fn(*gargs[i]))
+            cap_stream.synchronize()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for i in range(per_graph):
+                    L.check(fn(*gargs[i % copies]))
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // per_graph)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        t_graph = time.perf_counter() - t0
+        graph = {"ms_per_step": t_graph / (reps * per_graph) * 1e3,
+                 "value": work["flops"] * reps * per_graph / t_graph / 1e12, "calls_per_graph": per_graph}
+
+    # ---- roofline of the dominant kernel (the residual GEMM)
+    gemm_s = stage_ms["gemm"] / 1e3
+    mfma_peak = PEAK["mxfp4"] if wl.fmt == "mx" else PEAK["int8"]
+    t_mfma = work["flops"] / (mfma_peak * 1e12)
+    t_hbm = work["gemm_bytes"] / (PEAK["hbm"] * 1e9)
+    traffic = pmc_traffic(wl.name)
+    if t_mfma >= t_hbm:
+        ach = work["flops"] / gemm_s / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak}
+    else:
+        ach = work["gemm_bytes"] / gemm_s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]}
+    roof["traffic"] = traffic
+    roof["kernel"] = "k_gemm"
+    roof["avg_ms"] = stage_ms["gemm"]
+    roof["algorithmic_bytes"] = work["gemm_bytes"]
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_eager / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4" if wl.fmt == "mx" else "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "M": M, "N": N, "rank": wl.rank, "format": wl.fmt, "bits": wl.bits,
+                   "io_dtype": wl.dtype, "rotating_copies": copies},
+        "roofline": roof,
+        "call_gbs": work["call_bytes"] / (t_eager / args.steps) / 1e9,
+        "kernels_ms": stage_ms,
+        "graph": graph,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, s, prep)
+    print(json.dumps(out), flush=True)
+
+
+def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, workload, command):
+    """Per-dispatch HBM bytes of k_gemm from rocprofv3 counter CSVs, scaled by a copy kernel."""
+    import csv
+
+    def per_dispatch(path, counter, name_pred):
+        vals = []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter and name_pred(row.get("Kernel_Name", "")):
+                    vals.append(float(row["Counter_Value"]))
+        return sum(vals) / len(vals) if vals else float("nan"), len(vals)
+
+    is_gemm = lambda k: "k_gemm" in k  # noqa: E731
+    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    f_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE", is_gemm)
+    w_kib, nw = per_dispatch(write_csv, "WRITE_SIZE", is_gemm)
+    cf_kib, _ = per_dispatch(cfetch_csv, "FETCH_SIZE", is_copy)
+    cw_kib, _ = per_dispatch(cwrite_csv, "WRITE_SIZE", is_copy)
+    rf = copy_bytes / (cf_kib * 1024)
+    rw = copy_bytes / (cw_kib * 1024)
+    d = {"kernel": "k_gemm", "workload": workload, "source_sha": source_sha(GEMM_SRC),
+         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+         "copy_factor_fetch": rf, "copy_factor_write": rw,
+         "hbm_bytes_per_dispatch": f_kib * 1024 * rf + w_kib * 1024 * rw, "command": command}
+    print(json.dumps(d, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="1 toy f32 INT4, 2 INT4 W4A4 bf16 (default), 3 MXFP4 DiT attention, 4 MXFP4 MLP up, "
+                         "5 MXFP4 decode")
+    ap.add_argument("--rotate-mb", type=float, default=512.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_BYTES"))
+    ap.add_argument("--pmc-command", default="")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        from workloads import WORKLOADS
+
+        f, w_, cf, cw, cb = args.pmc_summary
+        pmc_summary(f, w_, cf, cw, float(cb), WORKLOADS[args.workload].name, args.pmc_command)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures the operator on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    run(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -210,6 +210,22 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
                               void* codes_out, int64_t ldc, void* scales_out, int64_t lds, float* sx_out,
                               void* workspace, size_t workspace_bytes, svdq_stream_t stream);
 
+/* --------------------------------------------------------------------------------------
+ * Kernel timing (profiling aid; not on any page). Between svdq_profile_begin and
+ * svdq_profile_end, each svdq_linear call records a HIP event pair around every kernel it
+ * launches, on the call's stream, for up to max_calls calls. Stages: 0 = per-tensor max
+ * pre-pass (INT), 1 = smooth+quantise+down-projection, 2 = split-K down reduction,
+ * 3 = residual GEMM + epilogue; a stage that did not run reads 0.
+ *   svdq_profile_begin: creates the events (host call; no device memory). EINVAL if
+ *     max_calls < 1 or a session is already open; EHIP if event creation fails.
+ *   svdq_profile_end: waits for the recorded events, writes ms[call * SVDQ_NSTAGES + stage]
+ *     for the n_calls (<= cap) calls recorded, destroys the events and closes the session.
+ * Not thread-safe: one session per process at a time.
+ * ------------------------------------------------------------------------------------ */
+#define SVDQ_NSTAGES 4
+int svdq_profile_begin(int max_calls);
+int svdq_profile_end(float* ms, int cap, int* n_calls);
+
 #ifdef __cplusplus
 }
 #endif

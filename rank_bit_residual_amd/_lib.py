@@ -30,7 +30,11 @@ SIGNATURES = {
                             c_sz, c_vp]),
     "svdq_quantize_activations": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                                           c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "svdq_profile_begin": (c_int, [c_int]),
+    "svdq_profile_end": (c_int, [ctypes.POINTER(ctypes.c_float), c_int, ctypes.POINTER(c_int)]),
 }
+NSTAGES = 4
+STAGE_NAMES = ("amax", "act_quant_down", "down_reduce", "gemm")
 
 SVDQ_OK, SVDQ_EINVAL, SVDQ_EDTYPE, SVDQ_EUNSUPPORTED, SVDQ_EHIP = 0, 1, 2, 3, 4
 SVDQ_F32, SVDQ_BF16, SVDQ_F64 = 0, 1, 2

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "launch.h"
 #include "svdq_internal.h"
@@ -45,6 +46,35 @@ void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]) 
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Kernel-timing session (svdq_profile_begin / svdq_profile_end).
+struct Profile {
+  bool open = false;
+  int max_calls = 0, calls = 0;
+  std::vector<hipEvent_t> ev;     // [call][stage][begin, end]
+  std::vector<uint8_t> recorded;  // [call][stage]: both events of the pair were recorded
+};
+Profile g_prof;
+
+struct StageTimer {
+  hipStream_t s;
+  int call = -1;
+  explicit StageTimer(hipStream_t s_) : s(s_) {
+    if (g_prof.open && g_prof.calls < g_prof.max_calls) call = g_prof.calls++;
+  }
+  hipEvent_t ev(int stage, int which) const { return g_prof.ev[((size_t)call * SVDQ_NSTAGES + stage) * 2 + which]; }
+  void begin(int stage) const {
+    if (call >= 0) hipEventRecord(ev(stage, 0), s);
+  }
+  void end(int stage) const {
+    if (call >= 0 && hipEventRecord(ev(stage, 1), s) == hipSuccess)
+      g_prof.recorded[(size_t)call * SVDQ_NSTAGES + stage] = 1;
+  }
+};
+
+// Clears an error left by an earlier, unrelated HIP call, so that the hipGetLastError()
+// after our own launch reports that launch only.
+inline void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return SVDQ_OK;
@@ -87,6 +117,7 @@ int svdq_smooth_inputs(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t
                        int64_t swm, int64_t swn, const float* scale, int dtype, void* xs_out, int64_t ldxs,
                        void* ws_out, int64_t ldws, svdq_stream_t stream) {
   clear_error();
+  clear_stale_hip_error();
   int st = check_dtype(dtype);
   if (st) return st;
   if (!scale) return set_error(SVDQ_EINVAL, "scale is NULL");
@@ -111,6 +142,7 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
                        void* out, int64_t ldo, float* s_out, void* workspace, size_t workspace_bytes,
                        svdq_stream_t stream) {
   clear_error();
+  clear_stale_hip_error();
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_format(SVDQ_FMT_INT, bits))) return st;
@@ -131,6 +163,7 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
                               int dtype, void* codes_out, int64_t ldc, void* scales_out, int64_t lds, float* sx_out,
                               void* workspace, size_t workspace_bytes, svdq_stream_t stream) {
   clear_error();
+  clear_stale_hip_error();
   int st = check_linear_dims(B, M, 1, 0, fmt, bits, dtype);
   if (st) return st;
   if (!x || !scale || !codes_out || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
@@ -180,6 +213,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
                 int bits, int dtype, void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                 svdq_stream_t stream) {
   clear_error();
+  clear_stale_hip_error();
   int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
   if (st) return st;
   if (!x || !blob || !y || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
@@ -201,10 +235,13 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   float* sx = (float*)(ws + woff[WS_SX]);
   const float* scale = (const float*)(bl + boff[SVDQ_SEC_SCALE]);
 
+  const StageTimer tm(s);
   // (a) + (b): smooth, quantise, down-project
   if (fmt == SVDQ_FMT_INT) {
+    tm.begin(0);
     if ((st = hip_status(launch_amax(x, B, M, ldx, 1, scale, dtype, amax, pl.amax_blocks, s), "activation max")))
       return st;
+    tm.end(0);
   }
   ActParams p{};
   p.x = x;
@@ -229,12 +266,16 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   p.k_chunk_len = pl.k_chunk_len;
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
   const int r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 128) : 1;
+  tm.begin(1);
   if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, r_chunks, s), "activation quantise launch")))
     return st;
+  tm.end(1);
   if (d.rp > 0 && pl.k_chunks > 1) {
+    tm.begin(2);
     if ((st = hip_status(launch_down_reduce(p.down_part, pl.k_chunks, (int)B, (int)d.rp, p.down, dtype, s),
                          "down-projection reduce launch")))
       return st;
+    tm.end(2);
   }
   // (c): residual GEMM + epilogue
   GemmParams g{};
@@ -256,7 +297,56 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.B = (int)B;
   g.N = (int)N;
   g.kstages = (int)(d.code_row_bytes() / 128);
-  return hip_status(launch_gemm(g, fmt, bits, dtype, s), "residual GEMM launch");
+  tm.begin(3);
+  st = hip_status(launch_gemm(g, fmt, bits, dtype, s), "residual GEMM launch");
+  tm.end(3);
+  return st;
+}
+
+int svdq_profile_begin(int max_calls) {
+  clear_error();
+  if (max_calls < 1) return set_error(SVDQ_EINVAL, "max_calls must be >= 1");
+  if (g_prof.open) return set_error(SVDQ_EINVAL, "a profiling session is already open");
+  g_prof.ev.assign((size_t)max_calls * SVDQ_NSTAGES * 2, nullptr);
+  for (auto& e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto& f : g_prof.ev)
+        if (f) hipEventDestroy(f);
+      g_prof.ev.clear();
+      return hip_status(r, "hipEventCreate");
+    }
+  }
+  g_prof.recorded.assign((size_t)max_calls * SVDQ_NSTAGES, 0);
+  g_prof.open = true;
+  g_prof.max_calls = max_calls;
+  g_prof.calls = 0;
+  return SVDQ_OK;
+}
+
+int svdq_profile_end(float* ms, int cap, int* n_calls) {
+  clear_error();
+  if (!g_prof.open) return set_error(SVDQ_EINVAL, "no profiling session is open");
+  const int n = std::min(g_prof.calls, cap);
+  for (int c = 0; c < n; c++) {
+    for (int k = 0; k < SVDQ_NSTAGES; k++) {
+      hipEvent_t a = g_prof.ev[((size_t)c * SVDQ_NSTAGES + k) * 2], b = g_prof.ev[((size_t)c * SVDQ_NSTAGES + k) * 2 + 1];
+      float v = 0.f;
+      if (g_prof.recorded[(size_t)c * SVDQ_NSTAGES + k]) {
+        hipError_t r = hipEventSynchronize(b);
+        if (r == hipSuccess) r = hipEventElapsedTime(&v, a, b);
+        if (r != hipSuccess) v = 0.f;
+      }
+      if (ms) ms[(size_t)c * SVDQ_NSTAGES + k] = v;
+    }
+  }
+  for (auto& e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.recorded.clear();
+  g_prof.open = false;
+  clear_stale_hip_error();
+  if (n_calls) *n_calls = n;
+  return SVDQ_OK;
 }
 
 }  // extern "C"
