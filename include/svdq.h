@@ -130,7 +130,10 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
  *   SVDQ_SEC_RCODES  uint8 [Np, Kp/2]  R^T codes, K-contiguous per output column n:
  *                    two 4-bit codes per byte, even k in the low nibble (MX: E2M1;
  *                    INT bits<=4: two's-complement nibbles) — or int8 [Np, Kp] for INT bits>4
- *   SVDQ_SEC_RSCALES MX: uint8 [Np, Kp/32] E8M0 bytes (e + 127) per 32-block of column n;
+ *   SVDQ_SEC_RSCALES MX: Np * Kp/32 E8M0 bytes (e + 127), one per 32-block of column n,
+ *                    stage-tiled: the byte of (n, block kb) sits at
+ *                    ((n/64) * (Kp/128) + kb/4) * 256 + (n%64) * 4 + kb%4
+ *                    (a 128-code stage's scales for 64 columns are 256 contiguous bytes);
  *                    INT: one float32 s_R
  *   SVDQ_SEC_L1T     dtype [rp, Kp]    L1^T (down-projection factor, transposed)
  *   SVDQ_SEC_L2T     dtype [Np, rp]    L2^T (up-projection factor, transposed)

@@ -25,6 +25,7 @@ HIP_FLAGS = [
 HIP_SOURCES = {
     "k_act.hip": ["-ffp-contract=off"],
     "k_gemm.hip": [],
+    "k_gemm_mx.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

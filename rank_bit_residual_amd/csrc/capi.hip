@@ -35,7 +35,7 @@ void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]) 
   };
   const int64_t B = p.B;
   sec(WS_CODES, B * d.code_row_bytes());
-  sec(WS_SCALES, d.fmt == SVDQ_FMT_MX ? B * d.mx_scale_row_bytes() : 0);
+  sec(WS_SCALES, d.fmt == SVDQ_FMT_MX ? round_up(B, 64) * d.mx_scale_row_bytes() : 0);  // stage-tiled
   sec(WS_DOWN, B * d.rp * (int64_t)dtype_size(d.dtype));
   sec(WS_PARTIAL, p.k_chunks > 1 ? (int64_t)p.k_chunks * B * d.rp * 4 : 0);
   sec(WS_AMAX, d.fmt == SVDQ_FMT_INT ? (int64_t)p.amax_blocks * 4 : 0);
@@ -254,6 +254,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   p.ldc = d.code_row_bytes();
   p.mxs = ws + woff[WS_SCALES];
   p.lds = d.mx_scale_row_bytes();
+  p.mxs_tiled = 1;
   p.amax_part = amax;
   p.n_amax = pl.amax_blocks;
   p.bits = bits;
@@ -282,11 +283,11 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.acodes = ws + woff[WS_CODES];
   g.lda = d.code_row_bytes();
   g.ascales = ws + woff[WS_SCALES];
-  g.ldas = d.mx_scale_row_bytes();
+  g.ascale_groups = (int)ceil_div(B, 64);
   g.wcodes = bl + boff[SVDQ_SEC_RCODES];
   g.ldw = d.code_row_bytes();
   g.wscales = bl + boff[SVDQ_SEC_RSCALES];
-  g.ldws = d.mx_scale_row_bytes();
+  g.kq = (int)(d.Kp / 128);
   g.sx = sx;
   g.sr = (const float*)(bl + boff[SVDQ_SEC_RSCALES]);
   g.down = ws + woff[WS_DOWN];
@@ -297,8 +298,16 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.B = (int)B;
   g.N = (int)N;
   g.kstages = (int)(d.code_row_bytes() / 128);
+  g.npad = (int)d.Np;
   tm.begin(3);
-  st = hip_status(launch_gemm(g, fmt, bits, dtype, s), "residual GEMM launch");
+  hipError_t ge = hipErrorNotSupported;
+  if (fmt == SVDQ_FMT_MX) {
+    g.kstages = (int)(d.code_row_bytes() / 64);  // 64-byte stages
+    ge = launch_gemm_mx_large(g, dtype, s);
+    if (ge == hipErrorNotSupported) g.kstages = (int)(d.code_row_bytes() / 128);
+  }
+  if (ge == hipErrorNotSupported) ge = launch_gemm(g, fmt, bits, dtype, s);
+  st = hip_status(ge, "residual GEMM launch");
   tm.end(3);
   return st;
 }

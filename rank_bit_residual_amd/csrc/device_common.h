@@ -76,6 +76,13 @@ __device__ inline u32 fp4_pack8(const float* v, float scale) {
   return r;
 }
 
+// Stage-tiled E8M0 layout used inside the library: for each group of 64 rows and each
+// 128-code K stage, the 64 rows' four block bytes are contiguous (256 bytes), so one wave
+// loads a stage's scales for 64 rows with four 64-byte requests.
+__host__ __device__ inline int64_t mx_scale_tiled_index(int64_t row, int64_t kb, int64_t kq) {
+  return (((row >> 6) * kq + (kb >> 2)) << 8) + ((row & 63) << 2) + (kb & 3);
+}
+
 // ---- per-tensor INT ---------------------------------------------------------------------
 // clamp(round_half_even(z / s), -qmax, qmax) with an IEEE division; s == 0 gives code 0.
 __device__ inline int int_code(float z, float s, float qmax) {

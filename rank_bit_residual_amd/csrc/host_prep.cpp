@@ -138,6 +138,12 @@ inline uint8_t e2m1_code(float z, int e) {
   return (uint8_t)(c | (std::signbit(z) ? 8 : 0));
 }
 
+// Stage-tiled E8M0 index (the device kernels' layout): for each 64-row group and each
+// 128-code K stage, the 64 rows' four block bytes are contiguous.
+inline int64_t mx_tiled(int64_t row, int64_t kb, int64_t kq) {
+  return (((row >> 6) * kq + (kb >> 2)) << 8) + ((row & 63) << 2) + (kb & 3);
+}
+
 int validate_prepare(int64_t M, int64_t N, int64_t ldw, int64_t rank, int fmt, int bits, int dtype) {
   int st = check_dtype(dtype);
   if (st) return st;
@@ -277,7 +283,6 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
   } else {
     // MXFP4 per column n of R, 32-element blocks along m
     uint8_t* sc = blob + off[SVDQ_SEC_RSCALES];
-    const int64_t srow = d.mx_scale_row_bytes();
     const int64_t nb = ceil_div(M, kMxBlock);
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++) {
@@ -286,7 +291,7 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
         float a = 0.f;
         for (int64_t m = m0; m < m1; m++) a = std::max(a, std::fabs(R[m * N + n]));
         const int e = mx_exponent(a);
-        sc[n * srow + b] = (uint8_t)(e + 127);
+        sc[mx_tiled(n, b, d.Kp / 128)] = (uint8_t)(e + 127);
         for (int64_t m = m0; m < m1; m++)
           codes[n * crow + m / 2] |= (uint8_t)(e2m1_code(R[m * N + n], e) << (4 * (m & 1)));
       }

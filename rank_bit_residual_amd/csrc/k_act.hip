@@ -204,7 +204,8 @@ __global__ __launch_bounds__(256) void k_act_quant(ActParams p) {
         w.z = fp4_pack8(xh + 16, sc);
         w.w = fp4_pack8(xh + 24, sc);
         *reinterpret_cast<uint4*>(p.codes + (int64_t)b * p.ldc + k / 2) = w;
-        p.mxs[(int64_t)b * p.lds + k / 32] = (uint8_t)(e + 127);
+        const int64_t si = p.mxs_tiled ? mx_scale_tiled_index(b, k / 32, p.Kp / 128) : (int64_t)b * p.lds + k / 32;
+        p.mxs[si] = (uint8_t)(e + 127);
       } else if constexpr (NIB) {
         u32 ws[4];
 #pragma unroll

@@ -54,14 +54,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     a_src[j] = p.acodes + (int64_t)ra * p.lda + ld_ch * 16;
     b_src[j] = p.wcodes + (int64_t)(n0 + ld_row + 32 * j) * p.ldw + ld_ch * 16;
   }
+  // scale bytes of one row for a 256-code stage: 4-block groups 2st and 2st+1 (tiled layout)
   const uint8_t* s_src = nullptr;
   if (MX) {
     if (t < BM) {
       int ra = m0 + t;
       ra = ra < p.B ? ra : p.B - 1;
-      s_src = p.ascales + (int64_t)ra * p.ldas;
+      s_src = p.ascales + mx_scale_tiled_index(ra, 0, p.kq);
     } else {
-      s_src = p.wscales + (int64_t)(n0 + t - BM) * p.ldws;
+      s_src = p.wscales + mx_scale_tiled_index(n0 + t - BM, 0, p.kq);
     }
   }
 
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       ra_[j] = *reinterpret_cast<const uint4*>(a_src[j] + st * SB);
       rb_[j] = *reinterpret_cast<const uint4*>(b_src[j] + st * SB);
     }
-    if (MX) rs_ = *reinterpret_cast<const u64*>(s_src + st * 8);
+    if (MX)
+      rs_ = (u64) * reinterpret_cast<const u32*>(s_src + (int64_t)(2 * st) * 256) |
+            ((u64) * reinterpret_cast<const u32*>(s_src + (int64_t)(2 * st + 1) * 256) << 32);
   };
   auto sstore = [&](int buf) {
 #pragma unroll

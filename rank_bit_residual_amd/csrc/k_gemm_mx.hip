@@ -1,0 +1,328 @@
+// Residual GEMM for MXFP4 at large batch on gfx950 (step (c) of the operator):
+//   Y = D( Q(X^) Q(R) + down L2 )
+// Q(X^) and Q(R) are E2M1 codes with one E8M0 scale per 32 elements along K; the product runs
+// on v_mfma_scale_f32_32x32x64_f8f6f4 (each lane's 32 K-contiguous FP4 values scaled by its own
+// E8M0 byte), fp32 accumulation; the up-projection down L2 runs on bf16 MFMAs into the same
+// accumulators before the single rounding to the output dtype.
+//
+// Pages: "SVDQuant Smoothing, Low-rank and Residual Quantization", "Formula and conventions"
+// item 3; "flashinfer.gemm.svdquant_linear" (residual GEMM with the low-rank up-projection in
+// its epilogue: prior art for this split); msModelSlim SVDQuant guide step 2 (MXFP4 per block).
+//
+// Structure: a BM x BN output tile per 256-thread block (2 x 2 waves). K advances in stages of
+// 128 codes (64 bytes per row). Stages land in a ring of NS LDS buffers through direct
+// global->LDS loads (global_load_lds_dwordx4 / _dword), issued NS-1 stages ahead; each wave
+// waits on its own vmcnt for the stage it is about to read, then one s_barrier makes every
+// wave's loads of that stage visible and releases the buffer read in the previous iteration.
+// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), so
+// the 16-byte reads of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
+#include "device_common.h"
+#include "launch.h"
+#include "../../include/svdq.h"
+
+namespace svdq {
+namespace dev {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN>
+struct MxCfg {
+  static constexpr int SB = 64;               // bytes per row per stage (128 FP4 codes)
+  static constexpr int TM = BM / 2, TN = BN / 2;  // per-wave tile
+  static constexpr int MT = TM / 32, NT = TN / 32;
+  static constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
+  static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // wave-wide 16-byte DMA loads
+  static_assert(A_INSTR % 4 == 0 && B_INSTR % 4 == 0, "tile rows must fill whole wave-wide loads");
+  static constexpr int A_PER_WAVE = A_INSTR / 4;
+  static constexpr int B_PER_WAVE = (B_INSTR + 3) / 4;
+  static constexpr int SCALE_BYTES = 1024;         // 256 rows x 4 bytes, per operand (padded)
+  static constexpr int STAGE = A_BYTES + B_PER_WAVE * 4 * 1024 + 2 * SCALE_BYTES;
+  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE + 2;  // per wave
+  static constexpr int NS = 4;    // LDS ring depth
+  static constexpr int DIST = 2;  // stages in flight ahead of the one being computed
+  static constexpr int SMEM = NS * STAGE;
+};
+
+__device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// s_waitcnt vmcnt(n) for a compile-time n (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int LPS, int NS>
+__device__ inline void wait_stage(int remaining_after) {
+  // remaining_after = number of later stages already issued (0 .. NS-2); loads complete in
+  // issue order, so allowing LPS * remaining_after outstanding leaves the wanted stage done.
+  if constexpr (NS >= 5) {
+    if (remaining_after >= 3) {
+      wait_vmcnt<LPS * 3>();
+      return;
+    }
+  }
+  if constexpr (NS >= 4) {
+    if (remaining_after >= 2) {
+      wait_vmcnt<LPS * 2>();
+      return;
+    }
+  }
+  if (remaining_after >= 1)
+    wait_vmcnt<LPS * 1>();
+  else
+    wait_vmcnt<0>();
+}
+
+template <class DT, int BM, int BN>
+__global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
+  typedef MxCfg<BM, BN> C;
+  typedef typename DT::T T;
+  extern __shared__ __align__(1024) uint8_t smem[];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // ---- tile order: XCD-aware (blocks i, i+8, ... share an XCD) and grouped by 4 row tiles
+  const int tiles_m = (p.B + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int tid = blockIdx.x;
+  if ((ntiles & 7) == 0) tid = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int GM = 4;
+  const int group = tid / (GM * tiles_n);
+  const int gm0 = group * GM;
+  const int gsz = (tiles_m - gm0) < GM ? (tiles_m - gm0) : GM;
+  const int in_g = tid - group * GM * tiles_n;
+  const int tm = gm0 + in_g % gsz, tn = in_g / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // ---- per-lane DMA sources (16-byte chunks) for this wave's share of a stage
+  const uint8_t* a_src[C::A_PER_WAVE];
+  int a_dst[C::A_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < C::A_PER_WAVE; j++) {
+    const int u = wave + 4 * j;  // instruction index: 16 rows x 64 bytes
+    const int q = u * 64 + lane;
+    const int row = q >> 2, phys = q & 3;
+    const int chunk = phys ^ ((row >> 2) & 3);
+    int gr = m0 + row;
+    gr = gr < p.B ? gr : p.B - 1;
+    a_src[j] = p.acodes + (int64_t)gr * p.lda + chunk * 16;
+    a_dst[j] = u * 1024;
+  }
+  const uint8_t* b_src[C::B_PER_WAVE];
+  int b_dst[C::B_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < C::B_PER_WAVE; j++) {
+    int u = wave + 4 * j;
+    const bool real = u < C::B_INSTR;
+    const int q = (real ? u : 0) * 64 + lane;
+    const int row = q >> 2, phys = q & 3;
+    const int chunk = phys ^ ((row >> 2) & 3);
+    int gr = n0 + row;
+    gr = gr < p.npad ? gr : p.npad - 1;
+    b_src[j] = p.wcodes + (int64_t)gr * p.ldw + chunk * 16;
+    b_dst[j] = C::A_BYTES + u * 1024;  // u >= B_INSTR lands in the padding after B
+  }
+  // scales (stage-tiled): wave w loads the 64-row group w of the A tile and of the B tile,
+  // 256 contiguous bytes per stage; groups past the data clamp to the last one (discarded)
+  int ga = (m0 >> 6) + wave;
+  ga = ga < p.ascale_groups ? ga : p.ascale_groups - 1;
+  const uint8_t* sa_src = p.ascales + ((int64_t)ga * p.kq << 8) + lane * 4;
+  int gb = (n0 >> 6) + (64 * wave < BN ? wave : 0);
+  gb = gb < (p.npad >> 6) ? gb : (p.npad >> 6) - 1;
+  const uint8_t* sb_src = p.wscales + ((int64_t)gb * p.kq << 8) + lane * 4;
+  const int s_off_a = C::A_BYTES + C::B_PER_WAVE * 4 * 1024;
+  const int s_off_b = s_off_a + C::SCALE_BYTES;
+
+  auto issue = [&](int st) {
+    uint8_t* base = smem + (st % C::NS) * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::A_PER_WAVE; j++)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + st * C::SB), (lds_ptr_t)(base + a_dst[j]), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::B_PER_WAVE; j++)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + st * C::SB), (lds_ptr_t)(base + b_dst[j]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(sa_src + st * 256), (lds_ptr_t)(base + s_off_a + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(sb_src + st * 256), (lds_ptr_t)(base + s_off_b + wave * 256), 4, 0, 0);
+  };
+
+  v16f acc[C::MT][C::NT];
+#pragma unroll
+  for (int i = 0; i < C::MT; i++)
+#pragma unroll
+    for (int j = 0; j < C::NT; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+  // Operand fragment of one 64-code K slice: A rows and B columns of this wave's tile read
+  // from the LDS stage buffer.
+  struct Frag {
+    v8i a[C::MT], b[C::NT];
+  };
+  // Scale words of a stage: four E8M0 bytes (one per 32-code block) per row / column.
+  struct Scales {
+    u32 a[C::MT], b[C::NT];
+  };
+  auto read_frag = [&](const uint8_t* base, int ks, Frag& f) {
+    const int ch = 2 * ks + g;  // this lane's 32-code K block within the stage
+#pragma unroll
+    for (int i = 0; i < C::MT; i++) {
+      const v4i a4 = *reinterpret_cast<const v4i*>(base + lds_swz(wm * C::TM + 32 * i + l32, ch));
+      f.a[i] = v8i{a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < C::NT; j++) {
+      const v4i b4 = *reinterpret_cast<const v4i*>(base + C::A_BYTES + lds_swz(wn * C::TN + 32 * j + l32, ch));
+      f.b[j] = v8i{b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
+    }
+  };
+  auto read_scales = [&](const uint8_t* base, Scales& sc) {
+#pragma unroll
+    for (int i = 0; i < C::MT; i++)
+      sc.a[i] = *reinterpret_cast<const u32*>(base + s_off_a + (wm * C::TM + 32 * i + l32) * 4);
+#pragma unroll
+    for (int j = 0; j < C::NT; j++)
+      sc.b[j] = *reinterpret_cast<const u32*>(base + s_off_b + (wn * C::TN + 32 * j + l32) * 4);
+  };
+  auto mma = [&](const Frag& f, const Scales& sc, int ks) {
+    const int sh = 8 * (2 * ks + g);
+#pragma unroll
+    for (int i = 0; i < C::MT; i++)
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 0,
+                                                                    (int)(sc.a[i] >> sh), 0, (int)(sc.b[j] >> sh));
+  };
+
+  // Pipeline: stage s+DIST is issued into the ring, the wave waits until its own loads of
+  // stage s have landed, one barrier publishes every wave's loads of stage s (and guarantees
+  // that the buffer refilled next iteration, last read at stage s-DIST, is no longer read),
+  // then both K slices of stage s are read from LDS and fed to 24 MFMAs. With NS = DIST + 2
+  // buffers a single barrier per stage suffices.
+  static_assert(C::NS >= C::DIST + 2, "ring too shallow for the prefetch distance");
+  const int nst = p.kstages;
+#pragma unroll
+  for (int s = 0; s < C::DIST; s++)
+    if (s < nst) issue(s);
+  Frag f0, f1;
+  for (int s = 0; s < nst; s++) {
+    if (s + C::DIST < nst) issue(s + C::DIST);
+    const int ahead = nst - 1 - s;  // stages issued after s
+    wait_stage<C::LOADS_PER_STAGE, C::DIST + 2>(ahead < C::DIST ? ahead : C::DIST);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* base = smem + (s % C::NS) * C::STAGE;
+    Scales sc;
+    read_scales(base, sc);
+    read_frag(base, 0, f0);
+    read_frag(base, 1, f1);
+    mma(f0, sc, 0);
+    mma(f1, sc, 1);
+    // Schedule: the scale words and slice 0's operands first, then slice 1's reads one per
+    // MFMA of slice 0, then the remaining MFMAs: one exposed LDS round trip per stage.
+    constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
+#pragma unroll
+    for (int q = 0; q < NR; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::MT * C::NT - NR, 0);
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- epilogue: up-projection on the matrix cores, one rounding, masked store
+  if (p.rp > 0) {
+    const T* down = reinterpret_cast<const T*>(p.down);
+    const T* l2t = reinterpret_cast<const T*>(p.l2t);
+    int drow[C::MT], bcol[C::NT];
+#pragma unroll
+    for (int i = 0; i < C::MT; i++) {
+      const int r = m0 + wm * C::TM + 32 * i + l32;
+      drow[i] = r < p.B ? r : p.B - 1;
+    }
+#pragma unroll
+    for (int j = 0; j < C::NT; j++) {
+      const int c = n0 + wn * C::TN + 32 * j + l32;
+      bcol[j] = c < p.npad ? c : p.npad - 1;
+    }
+    for (int kk = 0; kk < p.rp; kk += 16) {
+      v8bf av[C::MT], bv[C::NT];
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+        av[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)drow[i] * p.rp + kk + 8 * g));
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+        bv[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 8 * g));
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // Stage the rounded tile through the (now idle) LDS ring and write it with 16-byte stores:
+  // lanes hold 4-row x 1-column strips of each 32x32 accumulator, which as direct 2-byte stores
+  // would scatter the output over many partial cache lines.
+  static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
+  __syncthreads();
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+  for (int i = 0; i < C::MT; i++)
+#pragma unroll
+    for (int j = 0; j < C::NT; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int r = wm * C::TM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int c = wn * C::TN + 32 * j + l32;
+        tile[r * BN + c] = DT::from_f32(acc[i][j][v]);
+      }
+  __syncthreads();
+  T* y = reinterpret_cast<T*>(p.y);
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  const bool vec_ok = (p.ldy % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
+  for (int c = t; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = c - r * CPR;
+    const int row = m0 + r, col = n0 + cc * 8;
+    if (row >= p.B || col >= p.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * BN + cc * 8);
+    T* dst = y + (int64_t)row * p.ldy + col;
+    if (vec_ok && col + 8 <= p.N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+      for (int q = 0; q < 8 && col + q < p.N; q++) dst[q] = e[q];
+    }
+  }
+}
+
+}  // namespace dev
+
+using namespace dev;
+
+template <int BM, int BN>
+static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
+  typedef MxCfg<BM, BN> C;
+  const int tiles = ((p.B + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx<BF16, BM, BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  k_gemm_mx<BF16, BM, BN><<<tiles, 256, C::SMEM, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Large-batch MXFP4 path for bf16 inputs; returns hipErrorNotSupported when the shape or dtype
+// is not covered, so the caller falls back to the general kernel.
+hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
+  if (dtype != SVDQ_BF16 || p.B < 256) return hipErrorNotSupported;
+  if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, stream);
+  return launch_mx_t<256, 256>(p, stream);
+}
+
+}  // namespace svdq

@@ -14,8 +14,9 @@ struct ActParams {
   const float* scale;
   uint8_t* codes;  // [B][ldc] bytes, or NULL (down-projection only)
   int64_t ldc;
-  uint8_t* mxs;  // MX scales [B][lds]
+  uint8_t* mxs;  // MX scales: row-major [B][lds], or stage-tiled when mxs_tiled
   int64_t lds;
+  int mxs_tiled;
   const float* amax_part;  // INT: per-block maxima of |X^|
   int n_amax;
   int bits;
@@ -31,12 +32,12 @@ struct ActParams {
 struct GemmParams {
   const uint8_t* acodes;
   int64_t lda;
-  const uint8_t* ascales;
-  int64_t ldas;
+  const uint8_t* ascales;  // stage-tiled E8M0 bytes (see mx_scale_tiled_index)
+  int ascale_groups;       // 64-row groups of the activation scales
   const uint8_t* wcodes;
   int64_t ldw;
-  const uint8_t* wscales;
-  int64_t ldws;
+  const uint8_t* wscales;  // stage-tiled E8M0 bytes over npad rows
+  int kq;                  // Kp / 128: 128-code stages per row
   const float* sx;
   const float* sr;
   const void* down;
@@ -45,6 +46,7 @@ struct GemmParams {
   void* y;
   int64_t ldy;
   int B, N, kstages;
+  int npad;  // rows of the prepared weight (N rounded up); loads clamp to npad - 1
 };
 
 hipError_t launch_smooth(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t sxm, const void* w, int64_t N,
@@ -59,5 +61,7 @@ hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_bloc
 hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, void* down, int dtype,
                               hipStream_t stream);
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
+// Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
+hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
 
 }  // namespace svdq

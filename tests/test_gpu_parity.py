@@ -215,3 +215,39 @@ def test_strided_activations_match_contiguous():
     big = torch.zeros(64, 3072 + 64, dtype=torch.bfloat16, device=dev())
     big[:, 16:16 + 3072] = _g(x, "bf16")
     assert torch.equal(R.linear(big[:, 16:16 + 3072], p), R.linear(_g(x, "bf16"), p))
+
+
+# ----------------------------------------------------------------------------- large-batch MXFP4 kernel
+def _mx_case(B, M, N, rank, seed):
+    rng = np.random.default_rng(seed)
+    x = O.to_dtype(rng.standard_t(3, (B, M)), "bf16")
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 3)) @ rng.standard_normal((3, N)), "bf16")
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.25)
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(s), rank, 4, "mx", keep_factors=True)
+    y = R.linear(_g(x, "bf16"), p)
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "mx", 4, "bf16")
+    return O.rel_fro(_np(y), ref)
+
+
+@pytest.mark.parametrize("B,M,N,rank", [
+    (300, 512, 576, 32),    # ragged batch, N a multiple of 192 with a partial last padded block
+    (513, 320, 200, 7),     # N not a multiple of 192 (256-wide tiles), short K (2 stages < ring depth)
+    (256, 256, 1000, 64),   # one K stage pair, N tail
+    (1024, 1024, 384, 0),   # rank 0: no up-projection
+])
+def test_mx_large_batch_shapes(B, M, N, rank):
+    assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]
+
+
+def test_mx_exact_special_case_large_batch():
+    rng = np.random.default_rng(14)
+    B, M, N = 520, 320, 392
+    grid = O.E2M1_GRID
+    x = grid[rng.integers(0, 8, (B, M))] * np.where(rng.random((B, M)) < 0.5, -1, 1)
+    w = grid[rng.integers(0, 8, (M, N))] * np.where(rng.random((M, N)) < 0.5, -1, 1)
+    x[:, 0::32] = np.where(rng.random((B, M // 32)) < 0.5, 6.0, -4.0)
+    w[0::32, :] = np.where(rng.random((M // 32, N)) < 0.5, -6.0, 4.0)
+    p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx")
+    y = R.linear(_g(x, "bf16"), p)
+    assert np.array_equal(_bits(_np(y)), _bits(O.to_dtype(x @ w, "bf16")))

@@ -88,7 +88,9 @@ def test_residual_codes_bit_exact(name, rank, fmt, bits):
         c, sb = O.quantize_mx(res.T)
         want = O.pack_nibbles(c)
         nb = -(-M // 32)
-        scales = p.section(_lib.SEC_RSCALES)[: Np * (Kp // 32)].numpy().reshape(Np, Kp // 32)
+        tiled = p.section(_lib.SEC_RSCALES)[: Np * (Kp // 32)].numpy()
+        # stage-tiled layout: [Np/64][Kp/128][64 rows][4 blocks]
+        scales = tiled.reshape(Np // 64, Kp // 128, 64, 4).transpose(0, 2, 1, 3).reshape(Np, Kp // 32)
         assert np.array_equal(scales[:N, :nb], sb)
         assert not scales[N:].any() and not scales[:, nb:].any()
     assert np.array_equal(codes[:N, : want.shape[1]], want)
