@@ -137,6 +137,8 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
  *                    INT: one float32 s_R
  *   SVDQ_SEC_L1T     dtype [rp, Kp]    L1^T (down-projection factor, transposed)
  *   SVDQ_SEC_L2T     dtype [Np, rp]    L2^T (up-projection factor, transposed)
+ *   SVDQ_SEC_RECIP   float32 [M]       RN(1/scale[m]), or 0 where scale[m] lies outside
+ *                    [2^-90, 2^90]; the kernels use it for an exact fast x / scale
  * ------------------------------------------------------------------------------------ */
 enum {
   SVDQ_SEC_SCALE = 0,
@@ -144,8 +146,9 @@ enum {
   SVDQ_SEC_RSCALES = 2,
   SVDQ_SEC_L1T = 3,
   SVDQ_SEC_L2T = 4,
-  SVDQ_SEC_END = 5, /* offsets[SVDQ_SEC_END] = total blob bytes */
-  SVDQ_NSEC = 6
+  SVDQ_SEC_RECIP = 5,
+  SVDQ_SEC_END = 6, /* offsets[SVDQ_SEC_END] = total blob bytes */
+  SVDQ_NSEC = 7
 };
 
 /* Offsets of every section and the total size. Errors: EINVAL, EDTYPE. */

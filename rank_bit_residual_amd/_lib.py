@@ -39,7 +39,8 @@ STAGE_NAMES = ("amax", "act_quant_down", "down_reduce", "gemm")
 SVDQ_OK, SVDQ_EINVAL, SVDQ_EDTYPE, SVDQ_EUNSUPPORTED, SVDQ_EHIP = 0, 1, 2, 3, 4
 SVDQ_F32, SVDQ_BF16, SVDQ_F64 = 0, 1, 2
 SVDQ_FMT_INT, SVDQ_FMT_MX = 0, 1
-SEC_SCALE, SEC_RCODES, SEC_RSCALES, SEC_L1T, SEC_L2T, SEC_END = 0, 1, 2, 3, 4, 5
+SEC_SCALE, SEC_RCODES, SEC_RSCALES, SEC_L1T, SEC_L2T, SEC_RECIP, SEC_END = 0, 1, 2, 3, 4, 5, 6
+NSEC = 7
 
 _lib = None
 

@@ -167,7 +167,7 @@ class Prepared:
 
 
 def prepared_layout(M: int, N: int, rank: int, fmt: str = "int", bits: int = 4, dtype=torch.bfloat16) -> tuple:
-    off = (ctypes.c_int64 * 6)()
+    off = (ctypes.c_int64 * L.NSEC)()
     L.check(L.load().svdq_prepared_layout(M, N, rank, _fmt_code(fmt), bits, _DT[dtype], off))
     return tuple(int(v) for v in off)
 

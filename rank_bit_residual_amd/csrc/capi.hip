@@ -17,13 +17,16 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   LaunchPlan p;
   p.B = B;
   p.row_blocks = (int)ceil_div(B, 16);
-  // Split K across blocks when there are few row blocks, so that ~512 blocks stream L1^T.
-  const int64_t max_chunks = std::max<int64_t>(1, d.Kp / 512);
-  const int64_t want = std::max<int64_t>(1, ceil_div(512, p.row_blocks));
-  const int64_t chunks = std::min(max_chunks, want);
+  p.r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 64) : 1;
+  // Split K across blocks only when rows x low-rank chunks give fewer than ~256 blocks.
+  const int64_t per = (int64_t)p.row_blocks * p.r_chunks;
+  int64_t chunks = per >= 256 ? 1 : ceil_div(256, per);
+  chunks = std::min<int64_t>(chunks, std::max<int64_t>(1, d.Kp / 256));
   p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
   p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
-  p.amax_blocks = (int)std::min<int64_t>(B, 1024);
+  p.amax_cols = (int)ceil_div(d.M, 2048);
+  p.amax_rows = (int)std::max<int64_t>(1, std::min<int64_t>(B, ceil_div(512, p.amax_cols)));
+  p.amax_blocks = p.amax_cols * p.amax_rows;
   return p;
 }
 
@@ -183,7 +186,9 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
   hipStream_t s = (hipStream_t)stream;
   float* amax = (float*)(ws + off[WS_AMAX]);
   if (fmt == SVDQ_FMT_INT) {
-    if ((st = hip_status(launch_amax(x, B, M, ldx, 1, scale, dtype, amax, pl.amax_blocks, s), "activation max")))
+    if ((st = hip_status(launch_amax_smoothed(x, (int)B, (int)M, ldx, scale, nullptr, dtype, amax, pl.amax_cols,
+                                              pl.amax_rows, s),
+                         "activation max")))
       return st;
   }
   ActParams p{};
@@ -234,12 +239,15 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   float* amax = (float*)(ws + woff[WS_AMAX]);
   float* sx = (float*)(ws + woff[WS_SX]);
   const float* scale = (const float*)(bl + boff[SVDQ_SEC_SCALE]);
+  const float* recip = (const float*)(bl + boff[SVDQ_SEC_RECIP]);
 
   const StageTimer tm(s);
   // (a) + (b): smooth, quantise, down-project
   if (fmt == SVDQ_FMT_INT) {
     tm.begin(0);
-    if ((st = hip_status(launch_amax(x, B, M, ldx, 1, scale, dtype, amax, pl.amax_blocks, s), "activation max")))
+    if ((st = hip_status(launch_amax_smoothed(x, (int)B, (int)M, ldx, scale, recip, dtype, amax, pl.amax_cols,
+                                              pl.amax_rows, s),
+                         "activation max")))
       return st;
     tm.end(0);
   }
@@ -250,6 +258,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   p.M = (int)M;
   p.Kp = (int)d.Kp;
   p.scale = scale;
+  p.recip = recip;
   p.codes = ws + woff[WS_CODES];
   p.ldc = d.code_row_bytes();
   p.mxs = ws + woff[WS_SCALES];
@@ -266,9 +275,8 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   p.k_chunks = pl.k_chunks;
   p.k_chunk_len = pl.k_chunk_len;
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
-  const int r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 128) : 1;
   tm.begin(1);
-  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, r_chunks, s), "activation quantise launch")))
+  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, s), "activation quantise launch")))
     return st;
   tm.end(1);
   if (d.rp > 0 && pl.k_chunks > 1) {

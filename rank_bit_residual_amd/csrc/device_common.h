@@ -49,6 +49,23 @@ __device__ inline float smooth_value(float x, float s) {
   return DT::to_f32(DT::from_f32(x / s));
 }
 
+// Correctly rounded x / s from y = RN(1/s) (y = 0 marks a scale outside [2^-90, 2^90]).
+// q0 = RN(x y) is refined twice by Newton-Markstein steps q' = RN(q + r y) with the exact
+// remainder r = fma(-s, q, x): the first step makes q faithful, the second returns RN(x / s)
+// (Markstein 1990, IBM J. Res. Dev. 34(1); Muller et al., Handbook of Floating-Point
+// Arithmetic, the FMA-based division theorem). The theorem needs every intermediate in the
+// normal range, so tiny, huge or zero quotients (and flagged scales) take the IEEE division.
+__device__ inline float div_rn(float x, float s, float y) {
+  float q = x * y;
+  float r = __builtin_fmaf(-s, q, x);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-s, q, x);
+  q = __builtin_fmaf(r, y, q);
+  const float aq = fabsf(q), ax = fabsf(x);
+  if (!(aq >= 0x1p-90f && aq <= 0x1p90f && ax >= 0x1p-90f)) q = x / s;
+  return q;
+}
+
 // ---- MXFP4 ------------------------------------------------------------------------------
 // Shared exponent of a 32-element block from its max magnitude a: the smallest e with
 // a <= 6 * 2^e, clamped to [-127, 127] (E8M0 byte = e + 127). For normal a = 1.m * 2^E the

@@ -65,6 +65,7 @@ void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]) {
   sec(SVDQ_SEC_RSCALES, d.fmt == SVDQ_FMT_MX ? d.Np * d.mx_scale_row_bytes() : 16);
   sec(SVDQ_SEC_L1T, d.rp * d.Kp * (int64_t)dtype_size(d.dtype));
   sec(SVDQ_SEC_L2T, d.Np * d.rp * (int64_t)dtype_size(d.dtype));
+  sec(SVDQ_SEC_RECIP, d.M * 4);
   off[SVDQ_SEC_END] = o;
 }
 
@@ -257,6 +258,14 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
   split(ws, M, N, rank, dtype, L1, L2, R);
 
   std::memcpy(blob + off[SVDQ_SEC_SCALE], scale, (size_t)M * 4);
+  {
+    // correctly rounded reciprocals for the device's fast exact division (0 = use IEEE division)
+    float* rc = reinterpret_cast<float*>(blob + off[SVDQ_SEC_RECIP]);
+    for (int64_t m = 0; m < M; m++) {
+      const float sv = scale[m];
+      rc[m] = (sv >= 0x1p-90f && sv <= 0x1p90f) ? 1.0f / sv : 0.0f;
+    }
+  }
 
   uint8_t* codes = blob + off[SVDQ_SEC_RCODES];
   const int64_t crow = d.code_row_bytes();

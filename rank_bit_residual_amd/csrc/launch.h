@@ -12,6 +12,7 @@ struct ActParams {
   int64_t ldx;
   int B, M, Kp;
   const float* scale;
+  const float* recip;  // RN(1/scale) (0 = use IEEE division), or NULL for IEEE division everywhere
   uint8_t* codes;  // [B][ldc] bytes, or NULL (down-projection only)
   int64_t ldc;
   uint8_t* mxs;  // MX scales: row-major [B][lds], or stage-tiled when mxs_tiled
@@ -52,6 +53,10 @@ struct GemmParams {
 hipError_t launch_smooth(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t sxm, const void* w, int64_t N,
                          int64_t swm, int64_t swn, const float* scale, int dtype, void* xs, int64_t ldxs, void* ws,
                          int64_t ldws, hipStream_t stream);
+// Per-block maxima of |D(x / scale)| for the per-tensor INT scale, col_blocks = ceil(M / 2048)
+// by row_blocks blocks, into part[col_blocks * row_blocks].
+hipError_t launch_amax_smoothed(const void* x, int B, int M, int64_t ldx, const float* scale, const float* recip,
+                                int dtype, float* part, int col_blocks, int row_blocks, hipStream_t stream);
 // Per-block maxima of |z| (smoothed by `scale` when non-NULL) into part[nparts].
 hipError_t launch_amax(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, const float* scale,
                        int dtype, float* part, int nparts, hipStream_t stream);

@@ -50,10 +50,12 @@ void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]);
 enum { WS_CODES = 0, WS_SCALES, WS_DOWN, WS_PARTIAL, WS_AMAX, WS_SX, WS_END, WS_NSEC };
 struct LaunchPlan {
   int64_t B;
-  int row_blocks;   // activation row blocks of kernel (a)
+  int row_blocks;   // activation row blocks of kernel (a) (16 rows each)
+  int r_chunks;     // 64-wide low-rank column chunks of kernel (a)
   int k_chunks;     // split of K in kernel (a) (down-projection partials when > 1)
   int k_chunk_len;  // K columns per chunk (multiple of 128)
-  int amax_blocks;  // partial-max blocks of the INT pre-pass
+  int amax_cols, amax_rows;  // grid of the INT per-tensor max pre-pass
+  int amax_blocks;           // amax_cols * amax_rows partial maxima
 };
 LaunchPlan make_plan(const Dims& d, int64_t B);
 void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]);

@@ -38,7 +38,7 @@ def test_host_calls_report_errors_without_a_gpu():
     assert b"rank" in lib.svdq_last_error()
     assert lib.svdq_check_rank(4, 3, 3) == _lib.SVDQ_OK
     assert lib.svdq_last_error() == b""
-    off = (ctypes.c_int64 * 6)()
+    off = (ctypes.c_int64 * _lib.NSEC)()
     assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_MX, 3, _lib.SVDQ_BF16, off) == _lib.SVDQ_EINVAL
     assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F64, off) == _lib.SVDQ_EDTYPE
     assert lib.svdq_prepared_layout(64, 48, 8, _lib.SVDQ_FMT_INT, 9, _lib.SVDQ_F32, off) == _lib.SVDQ_EINVAL
