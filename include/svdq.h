@@ -135,7 +135,12 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
  *                    ((n/64) * (Kp/128) + kb/4) * 256 + (n%64) * 4 + kb%4
  *                    (a 128-code stage's scales for 64 columns are 256 contiguous bytes);
  *                    INT: one float32 s_R
- *   SVDQ_SEC_L1T     dtype [rp, Kp]    L1^T (down-projection factor, transposed)
+ *   SVDQ_SEC_L1T     dtype, rp * Kp    L1^T (down-projection factor, transposed), tiled for
+ *                    the matrix cores: with E = 16 / sizeof(dtype) elements per 16 bytes,
+ *                    element (t, k) sits at ((t/16) * (Kp/128) + k/128) * 2048
+ *                    + ((((k%32)/E) * 4 + (k%128)/32) * 16 + t%16) * E + k%E
+ *                    (each 16-row x 128-K tile is 2048 contiguous elements, ordered so one
+ *                    wave reads a K-slice of it with one 1 KB request)
  *   SVDQ_SEC_L2T     dtype [Np, rp]    L2^T (up-projection factor, transposed)
  *   SVDQ_SEC_RECIP   float32 [M]       RN(1/scale[m]), or 0 where scale[m] lies outside
  *                    [2^-90, 2^90]; the kernels use it for an exact fast x / scale

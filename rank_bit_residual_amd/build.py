@@ -26,6 +26,7 @@ HIP_SOURCES = {
     "k_act.hip": ["-ffp-contract=off"],
     "k_gemm.hip": [],
     "k_gemm_mx.hip": [],
+    "k_gemm_decode.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

@@ -311,7 +311,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   hipError_t ge = hipErrorNotSupported;
   if (fmt == SVDQ_FMT_MX) {
     g.kstages = (int)(d.code_row_bytes() / 64);  // 64-byte stages
-    ge = launch_gemm_mx_large(g, dtype, s);
+    ge = B <= 64 ? launch_gemm_mx_decode(g, dtype, s) : launch_gemm_mx_large(g, dtype, s);
     if (ge == hipErrorNotSupported) g.kstages = (int)(d.code_row_bytes() / 128);
   }
   if (ge == hipErrorNotSupported) ge = launch_gemm(g, fmt, bits, dtype, s);

@@ -306,11 +306,17 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
       }
     }
   }
-  // low-rank factors, transposed and zero-padded: L1^T [rp, Kp], L2^T [Np, rp]
+  // low-rank factors, transposed and zero-padded: L1^T [rp, Kp] in 16x128 matrix-core tiles,
+  // L2^T [Np, rp] row-major
   void* l1t = blob + off[SVDQ_SEC_L1T];
   void* l2t = blob + off[SVDQ_SEC_L2T];
+  const int64_t E = 16 / dtype_size(dtype);
   for (int64_t t = 0; t < rank; t++)
-    for (int64_t m = 0; m < M; m++) store_exact(l1t, t * d.Kp + m, dtype, L1[m * rank + t]);
+    for (int64_t m = 0; m < M; m++) {
+      const int64_t tile = (t / 16) * (d.Kp / 128) + m / 128;
+      const int64_t in_tile = ((((m % 32) / E) * 4 + (m % 128) / 32) * 16 + t % 16) * E + m % E;
+      store_exact(l1t, tile * 2048 + in_tile, dtype, L1[m * rank + t]);
+    }
   for (int64_t n = 0; n < N; n++)
     for (int64_t t = 0; t < rank; t++) store_exact(l2t, n * d.rp + t, dtype, L2[t * N + n]);
 

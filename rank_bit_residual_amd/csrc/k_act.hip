@@ -149,6 +149,8 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
 // shared exponent and codes stay inside the lane. For the down-projection the lane feeds the
 // same 32 values to the matrix cores: 16x16x32 bf16 MFMAs in four K-slices of 8 (the B
 // operand lane (n, g) supplies L1^T[n] at the same K offsets, so the K order is consistent).
+// L1^T is stored in 16-row x 128-K tiles ordered by (K-slice, block, row), so the B operand of
+// one MFMA is a single contiguous 1 KB wave load.
 constexpr int ACT_WAVES = 8;
 constexpr int ACT_RCHUNK = 64;
 
@@ -327,26 +329,35 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
     }
     if (nbl > 0) {
       if constexpr (DT::is_bf16) {
+        v4i bw[ACT_RCHUNK / 16][4];
+#pragma unroll
+        for (int n = 0; n < ACT_RCHUNK / 16; n++)
+          if (n < nbl) {
+            const T* tile = l1t + ((int64_t)(rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + lane * 8;
+#pragma unroll
+            for (int s = 0; s < 4; s++) bw[n][s] = *reinterpret_cast<const v4i*>(tile + s * 512);
+          }
 #pragma unroll
         for (int s = 0; s < 4; s++) {
           const v8bf av = __builtin_bit_cast(v8bf, v4i{(int)xb[4 * s], (int)xb[4 * s + 1], (int)xb[4 * s + 2], (int)xb[4 * s + 3]});
 #pragma unroll
-          for (int n = 0; n < ACT_RCHUNK / 16; n++) {
-            if (n < nbl) {
-              const T* lr = l1t + (int64_t)(rbase + 16 * n + i) * p.Kp + k + 8 * s;
-              const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(lr));
-              acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
-            }
-          }
+          for (int n = 0; n < ACT_RCHUNK / 16; n++)
+            if (n < nbl) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, bw[n][s]), acc[n], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int n = 0; n < ACT_RCHUNK / 16; n++) {
           if (n < nbl) {
-            const float* lr = reinterpret_cast<const float*>(l1t) + (int64_t)(rbase + 16 * n + i) * p.Kp + k;
+            const float* tile = reinterpret_cast<const float*>(l1t) +
+                                ((int64_t)(rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + lane * 4;
 #pragma unroll
-            for (int s = 0; s < 32; s++)
-              acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xb[s]), lr[s], acc[n], 0, 0, 0);
+            for (int c = 0; c < 8; c++) {
+              const float4 lr = *reinterpret_cast<const float4*>(tile + c * 256);
+              const float l4[4] = {lr.x, lr.y, lr.z, lr.w};
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xb[4 * c + e]), l4[e], acc[n], 0, 0, 0);
+            }
           }
         }
       }

@@ -251,3 +251,14 @@ def test_mx_exact_special_case_large_batch():
     p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx")
     y = R.linear(_g(x, "bf16"), p)
     assert np.array_equal(_bits(_np(y)), _bits(O.to_dtype(x @ w, "bf16")))
+
+
+# ----------------------------------------------------------------------------- decode-batch MXFP4 kernel
+@pytest.mark.parametrize("B,M,N,rank", [
+    (1, 4608, 1000, 32),    # single row; each wave gets 9 K stages (one batch of 8 + a tail)
+    (17, 2048, 520, 16),    # two 16-row tiles, the second with one live row
+    (33, 4352, 300, 128),   # four row tiles; uneven K quarters (8 and 9 stages)
+    (64, 1024, 4104, 0),    # full 64 rows, rank 0, N tail inside the last 32-column block
+])
+def test_mx_decode_batch_shapes(B, M, N, rank):
+    assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]

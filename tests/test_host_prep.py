@@ -54,7 +54,10 @@ def _sections(p):
     rb = Kp // 2 if nib else Kp
     codes = p.section(_lib.SEC_RCODES)[: Np * rb].numpy().reshape(Np, rb)
     dt = np.float32 if p.dtype == torch.float32 else np.uint16
-    l1t = p.section(_lib.SEC_L1T).numpy().view(dt)[: rp * Kp].reshape(rp, Kp)
+    E = 16 // np.dtype(dt).itemsize
+    # L1^T tiles: [rp/16][Kp/128][32/E K-slices][4 blocks][16 rows][E]
+    tiles = p.section(_lib.SEC_L1T).numpy().view(dt)[: rp * Kp].reshape(rp // 16, Kp // 128, 32 // E, 4, 16, E)
+    l1t = tiles.transpose(0, 4, 1, 3, 2, 5).reshape(rp, Kp)
     l2t = p.section(_lib.SEC_L2T).numpy().view(dt)[: Np * rp].reshape(Np, rp)
     return codes, l1t, l2t, Kp, Np, rp, nib
 
