@@ -180,8 +180,9 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
  * Workspace of svdq_linear / svdq_quantize_activations: device scratch the caller
  * allocates once (any contents; nothing needs zeroing) and may reuse across calls that are
  * ordered on one stream. Holds activation codes [B, Kp/2] (int8 [B,Kp] for INT bits>4),
- * MX scales [B, Kp/32], the down-projection [B, rp], its split-K partials and the
- * per-tensor INT maxima. Errors: EINVAL, EDTYPE.
+ * MX scales [B, Kp/32], the down-projection [B, rp], its split-K partials, the
+ * per-tensor INT maxima and (svdq_quantize_activations) the reciprocals of the scale.
+ * Errors: EINVAL, EDTYPE.
  * ------------------------------------------------------------------------------------ */
 int svdq_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
                          size_t* bytes_out);
@@ -215,6 +216,8 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
  *   scales_out (MX): [B, lds] E8M0 bytes, ceil(M/32) meaningful per row, lds >= Kp/32.
  *   sx_out (INT): device float* receiving s_x. Unused outputs may be NULL.
  *   workspace: >= svdq_workspace_bytes(B, M, 1, 0, fmt, bits, dtype).
+ *   Runs the same kernels as svdq_linear's step (a), with the reciprocals of the scale
+ *   (the prepared RECIP section) computed on the device first.
  * ------------------------------------------------------------------------------------ */
 int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, const float* scale,
                               int fmt, int bits, int dtype,

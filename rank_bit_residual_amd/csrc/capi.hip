@@ -18,10 +18,11 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   p.B = B;
   p.row_blocks = (int)ceil_div(B, 16);
   p.r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 64) : 1;
-  // Split K across blocks only when rows x low-rank chunks give fewer than ~256 blocks.
+  // Split K across blocks only when rows x low-rank chunks give fewer than ~256 blocks, and
+  // never below one 128-wide step per wave of a block (8 waves: 1024 K per chunk).
   const int64_t per = (int64_t)p.row_blocks * p.r_chunks;
   int64_t chunks = per >= 256 ? 1 : ceil_div(256, per);
-  chunks = std::min<int64_t>(chunks, std::max<int64_t>(1, d.Kp / 256));
+  chunks = std::min<int64_t>(chunks, std::max<int64_t>(1, ceil_div(d.Kp, 1024)));
   p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
   p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
   p.amax_cols = (int)ceil_div(d.M, 2048);
@@ -43,6 +44,7 @@ void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]) 
   sec(WS_PARTIAL, p.k_chunks > 1 ? (int64_t)p.k_chunks * B * d.rp * 4 : 0);
   sec(WS_AMAX, d.fmt == SVDQ_FMT_INT ? (int64_t)p.amax_blocks * 4 : 0);
   sec(WS_SX, 16);
+  sec(WS_RECIP, d.Kp * 4);  // svdq_quantize_activations: RN(1/scale) computed on the device
   off[WS_END] = o;
 }
 
@@ -185,8 +187,10 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
   float* amax = (float*)(ws + off[WS_AMAX]);
+  float* recip = (float*)(ws + off[WS_RECIP]);
+  if ((st = hip_status(launch_reciprocals(scale, (int)M, recip, s), "reciprocal launch"))) return st;
   if (fmt == SVDQ_FMT_INT) {
-    if ((st = hip_status(launch_amax_smoothed(x, (int)B, (int)M, ldx, scale, nullptr, dtype, amax, pl.amax_cols,
+    if ((st = hip_status(launch_amax_smoothed(x, (int)B, (int)M, ldx, scale, recip, dtype, amax, pl.amax_cols,
                                               pl.amax_rows, s),
                          "activation max")))
       return st;
@@ -198,6 +202,7 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
   p.M = (int)M;
   p.Kp = (int)d.Kp;
   p.scale = scale;
+  p.recip = recip;
   p.codes = (uint8_t*)codes_out;
   p.ldc = ldc;
   p.mxs = (uint8_t*)scales_out;

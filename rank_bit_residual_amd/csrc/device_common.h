@@ -66,6 +66,36 @@ __device__ inline float div_rn(float x, float s, float y) {
   return q;
 }
 
+// Round two floats to bfloat16 (nearest, ties to even; v_cvt_pk_bf16_f32), packed low-first.
+__device__ inline u32 pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(u32, __builtin_convertvector(f2{a, b}, bf2));
+}
+
+// True when t = RN(x * RN(1/s)) may round to a different bfloat16 than RN_f32(x / s):
+// t within 8 ulps of a bf16 rounding midpoint (low 16 bits in [0x7FF8, 0x8007]), or t not a
+// normal number (zero, subnormal, infinite, NaN) while x is nonzero. The two differ by at
+// most 3 ulps when x * RN(1/s) is a normal product of normal factors.
+__device__ inline bool bf16_fast_risky(float t, float x) {
+  const u32 u = __float_as_uint(t);
+  const bool near_mid = ((u + 8u) & 0xFFF0u) == 0x8000u;
+  // class mask: every class except -normal (bit 3) and +normal (bit 8)
+  const bool not_normal = __builtin_amdgcn_classf(t, 0x2F7) && x != 0.f;
+  return near_mid || not_normal;
+}
+
+// RN_bf16(RN_f32(x / s)) from y = RN(1/s) (0 for a scale outside [2^-90, 2^90]), as a float:
+// the product RN(x y) unless bf16_fast_risky flags it, then the correctly rounded division.
+__device__ inline float smooth_bf16(float x, float s, float y) {
+  float t = x * y;
+  if (bf16_fast_risky(t, x)) {
+    asm volatile("");  // rarely taken: keep it a branch
+    t = div_rn(x, s, y);
+  }
+  return t;
+}
+
 // ---- MXFP4 ------------------------------------------------------------------------------
 // Shared exponent of a 32-element block from its max magnitude a: the smallest e with
 // a <= 6 * 2^e, clamped to [-127, 127] (E8M0 byte = e + 127). For normal a = 1.m * 2^E the
@@ -90,6 +120,18 @@ __device__ inline u32 fp4_pack8(const float* v, float scale) {
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+  return r;
+}
+
+// The same from eight bfloat16 values (four packed pairs, element 2p low in pair p):
+// v_cvt_scalef32_pk_fp4_bf16 converts the exact bf16 values with the same rounding.
+__device__ inline u32 fp4_pack8_bf16(const u32* pairs, float scale) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  u32 r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf2, pairs[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf2, pairs[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf2, pairs[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf2, pairs[3]), scale, 3);
   return r;
 }
 

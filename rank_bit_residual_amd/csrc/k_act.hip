@@ -24,7 +24,14 @@ __global__ void k_smooth_x(const typename DT::T* __restrict__ x, int64_t B, int6
   const int64_t n = B * M;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t b = i / M, m = i - b * M;
-    xs[b * ldxs + m] = DT::from_f32(DT::to_f32(x[b * sxb + m * sxm]) / scale[m]);
+    const float v = DT::to_f32(x[b * sxb + m * sxm]), s = scale[m];
+    if constexpr (DT::is_bf16) {
+      // the same rounding path as the operator's activation kernel
+      const float y = (s >= 0x1p-90f && s <= 0x1p90f) ? 1.0f / s : 0.f;
+      xs[b * ldxs + m] = DT::from_f32(smooth_bf16(v, s, y));
+    } else {
+      xs[b * ldxs + m] = DT::from_f32(v / s);
+    }
   }
 }
 
@@ -151,6 +158,10 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
 // operand lane (n, g) supplies L1^T[n] at the same K offsets, so the K order is consistent).
 // L1^T is stored in 16-row x 128-K tiles ordered by (K-slice, block, row), so the B operand of
 // one MFMA is a single contiguous 1 KB wave load.
+//
+// Steps that lie wholly inside [0, M) with 16-byte aligned rows run a branch-free body (all
+// of the step's loads are independent and issue together); only the tail step and the zero
+// padding up to Kp take the guarded body.
 constexpr int ACT_WAVES = 8;
 constexpr int ACT_RCHUNK = 64;
 
@@ -183,14 +194,200 @@ __device__ inline void load_row32(const typename DT::T* __restrict__ xrow, int k
   }
 }
 
-// 8 consecutive entries of a per-channel float array (scale or reciprocal); `pad` past M.
-__device__ inline void load8(const float* __restrict__ a, int k, int M, float pad, float* v) {
-  if (k + 8 <= M) {
-    const float4 u = *reinterpret_cast<const float4*>(a + k), w = *reinterpret_cast<const float4*>(a + k + 4);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+// n consecutive floats of a per-channel array (scale or reciprocal); `pad` past M unless FULL.
+template <bool FULL>
+__device__ inline void load_chan(const float* __restrict__ a, int k, int M, float pad, float* v) {
+  if (FULL) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const float4 u = *reinterpret_cast<const float4*>(a + k + 4 * q);
+      v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = (k + j < M) ? a[k + j] : pad;
+    for (int j = 0; j < 32; j++) v[j] = (k + j < M) ? a[k + j] : pad;
+  }
+}
+
+// Per-lane constants of a block.
+struct ActLane {
+  int lane, i, g, b, rbase, nbl;
+  bool do_codes;
+  float sx, ysx, qmax;
+};
+
+// One 128-wide K step of one wave (see the kernel comment).
+template <class DT, int FMT, bool NIB, bool FULL>
+__device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
+                                         int k0, v4f* acc) {
+  typedef typename DT::T T;
+  constexpr int RW = DT::is_bf16 ? 16 : 32;
+  const int k = k0 + 32 * L.g;
+  const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
+
+  u32 raw[RW];
+  if (FULL) {
+    const uint4* src = reinterpret_cast<const uint4*>(xrow + k);
+#pragma unroll
+    for (int q = 0; q < RW / 4; q++) {
+      const uint4 w = src[q];
+      raw[4 * q] = w.x; raw[4 * q + 1] = w.y; raw[4 * q + 2] = w.z; raw[4 * q + 3] = w.w;
+    }
+  } else {
+    load_row32<DT>(xrow, k, p.M, p.x_vec_ok, raw);
+  }
+  float s32[32], y32[32];
+  load_chan<FULL>(p.scale, k, p.M, 1.f, s32);
+  load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
+  // B operands of the down-projection for this step
+  constexpr int NB = ACT_RCHUNK / 16;
+  // (bf16: loaded with the step's other loads; f32 loads them at the MFMAs to save registers)
+  v4i bw[NB][4];
+  if (DT::is_bf16 && L.nbl > 0) {
+#pragma unroll
+    for (int n = 0; n < NB; n++)
+      if (n < L.nbl) {
+        const T* tile = l1t + ((int64_t)(L.rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + L.lane * (16 / sizeof(T));
+#pragma unroll
+        for (int c = 0; c < 4; c++) bw[n][c] = *reinterpret_cast<const v4i*>(tile + c * 512);
+      }
+  }
+
+  // X^ = D(x / scale); xb: X^ as stored (bf16 pairs or f32 bits); amax: max |X^| before the
+  // final rounding to the dtype (rounding is monotone, so it rounds to max |X^|).
+  u32 xb[RW];
+  float amax = 0.f;
+  if constexpr (DT::is_bf16) {
+    // bf16: X^ = RN_bf16(RN_f32(x / s)). The product t = RN(x * RN(1/s)) lies within 3 f32
+    // ulps of RN_f32(x / s), so RN_bf16(t) is already exact unless t sits within 8 ulps of a
+    // bf16 rounding midpoint (low 16 bits near 0x8000), or t is not a normal number while x is
+    // nonzero (underflow, or a scale whose reciprocal was not stored); those rare elements
+    // take the correctly rounded division.
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      const float x0 = __uint_as_float(raw[j / 2] << 16), x1 = __uint_as_float(raw[j / 2] & 0xFFFF0000u);
+      const float t0 = smooth_bf16(x0, s32[j], y32[j]), t1 = smooth_bf16(x1, s32[j + 1], y32[j + 1]);
+      amax = fmaxf(amax, fmaxf(fabsf(t0), fabsf(t1)));
+      xb[j / 2] = pack_bf16x2(t0, t1);
+    }
+    amax = __uint_as_float((u32)BF16::from_f32(amax) << 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      float x0, x1;
+      if constexpr (DT::is_bf16) {
+        x0 = __uint_as_float(raw[j / 2] << 16);
+        x1 = __uint_as_float(raw[j / 2] & 0xFFFF0000u);
+      } else {
+        x0 = __uint_as_float(raw[j]);
+        x1 = __uint_as_float(raw[j + 1]);
+      }
+      const float q0 = div_rn(x0, s32[j], y32[j]);
+      const float q1 = div_rn(x1, s32[j + 1], y32[j + 1]);
+      if constexpr (DT::is_bf16) {
+        const u32 pk = pack_bf16x2(q0, q1);
+        xb[j / 2] = pk;
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(pk << 16)), fabsf(__uint_as_float(pk & 0xFFFF0000u))));
+      } else {
+        xb[j] = __float_as_uint(q0);
+        xb[j + 1] = __float_as_uint(q1);
+        amax = fmaxf(amax, fmaxf(fabsf(q0), fabsf(q1)));
+      }
+    }
+  }
+  auto val = [&](int j) -> float {
+    if constexpr (DT::is_bf16)
+      return (j & 1) ? __uint_as_float(xb[j / 2] & 0xFFFF0000u) : __uint_as_float(xb[j / 2] << 16);
+    else
+      return __uint_as_float(xb[j]);
+  };
+  // INT code of z: clamp(rint(RN_f32(z / s_x))). With the fast product t = RN(z * RN(1/s_x))
+  // (|t| <= qmax + 1, so 8 ulps < 2^-14) rint(t) is exact unless t lies within 2^-14 of a
+  // half-integer; those take the correctly rounded division.
+  const bool int_fast = L.ysx != 0.f;
+  auto int_code_of = [&](float z) -> int {
+    if (L.sx == 0.f) return 0;
+    float d;
+    if (int_fast) {
+      d = z * L.ysx;
+      if (fabsf(d - __builtin_rintf(d)) >= 0.5f - 0x1p-14f) {
+        asm volatile("");  // rarely taken: keep it a branch
+        d = div_rn(z, L.sx, L.ysx);
+      }
+    } else {
+      d = div_rn(z, L.sx, L.ysx);
+    }
+    return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(d), -L.qmax, L.qmax);
+  };
+  if (L.do_codes && L.b < p.B) {
+    if constexpr (FMT == SVDQ_FMT_MX) {
+      const int e = mx_exponent(amax);
+      const float sc = pow2f(e);
+      u32 w4[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if constexpr (DT::is_bf16) {
+          w4[q] = fp4_pack8_bf16(&xb[4 * q], sc);
+        } else {
+          float v[8];
+#pragma unroll
+          for (int h = 0; h < 8; h++) v[h] = val(8 * q + h);
+          w4[q] = fp4_pack8(v, sc);
+        }
+      }
+      *reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k / 2) = uint4{w4[0], w4[1], w4[2], w4[3]};
+      const int64_t si = p.mxs_tiled ? mx_scale_tiled_index(L.b, k / 32, p.Kp / 128) : (int64_t)L.b * p.lds + k / 32;
+      p.mxs[si] = (uint8_t)(e + 127);
+    } else if constexpr (NIB) {
+      u32 ws[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        u32 r = 0;
+#pragma unroll
+        for (int h = 0; h < 8; h++) r |= (u32)(int_code_of(val(8 * q + h)) & 0xF) << (4 * h);
+        ws[q] = r;
+      }
+      *reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k / 2) = uint4{ws[0], ws[1], ws[2], ws[3]};
+    } else {
+      u32 ws[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        u32 r = 0;
+#pragma unroll
+        for (int h = 0; h < 4; h++) r |= (u32)(int_code_of(val(4 * q + h)) & 0xFF) << (8 * h);
+        ws[q] = r;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k);
+      dst[0] = uint4{ws[0], ws[1], ws[2], ws[3]};
+      dst[1] = uint4{ws[4], ws[5], ws[6], ws[7]};
+    }
+  }
+  if (L.nbl > 0) {
+    if constexpr (DT::is_bf16) {
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const v8bf av = __builtin_bit_cast(v8bf, v4i{(int)xb[4 * s], (int)xb[4 * s + 1], (int)xb[4 * s + 2], (int)xb[4 * s + 3]});
+#pragma unroll
+        for (int n = 0; n < NB; n++)
+          if (n < L.nbl) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, bw[n][s]), acc[n], 0, 0, 0);
+      }
+    } else {
+      // f32: 16x16x4 MFMAs; K-slice c of the tile holds k0 + 32 g + 4 c + e for e < 4
+#pragma unroll
+      for (int n = 0; n < NB; n++)
+        if (n < L.nbl) {
+          const float* tile = reinterpret_cast<const float*>(l1t) +
+                              ((int64_t)(L.rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + L.lane * 4;
+#pragma unroll
+          for (int c = 0; c < 8; c++) {
+            const float4 l4 = *reinterpret_cast<const float4*>(tile + c * 256);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xb[4 * c + e]), lv[e], acc[n], 0, 0, 0);
+          }
+        }
+    }
   }
 }
 
@@ -199,180 +396,59 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   typedef typename DT::T T;
   constexpr int NW = ACT_WAVES;
   __shared__ float red[NW][16][ACT_RCHUNK];
-  __shared__ float sh[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = lane & 15, g = lane >> 4;
+  ActLane L;
+  L.lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  L.i = L.lane & 15;
+  L.g = L.lane >> 4;
   const int row0 = blockIdx.x * 16;
-  const int b = row0 + i;
-  const int bl = b < p.B ? b : p.B - 1;
+  L.b = row0 + L.i;
+  const int bl = L.b < p.B ? L.b : p.B - 1;
   const int kbeg = blockIdx.y * p.k_chunk_len;
   const int kend = kbeg + p.k_chunk_len < p.Kp ? kbeg + p.k_chunk_len : p.Kp;
-  const int rbase = blockIdx.z * ACT_RCHUNK;
-  const int nbl = p.rp > rbase ? ((p.rp - rbase) >= ACT_RCHUNK ? ACT_RCHUNK / 16 : (p.rp - rbase) / 16) : 0;
-  const bool do_codes = blockIdx.z == 0 && p.codes != nullptr;
+  L.rbase = blockIdx.z * ACT_RCHUNK;
+  L.nbl = p.rp > L.rbase ? ((p.rp - L.rbase) >= ACT_RCHUNK ? ACT_RCHUNK / 16 : (p.rp - L.rbase) / 16) : 0;
+  L.do_codes = blockIdx.z == 0 && p.codes != nullptr;
   const T* __restrict__ xrow = reinterpret_cast<const T*>(p.x) + (int64_t)bl * p.ldx;
-  const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
 
-  float sx = 0.f, ysx = 0.f, qmax = 0.f;
+  L.sx = 0.f;
+  L.ysx = 0.f;
+  L.qmax = 0.f;
   if constexpr (FMT == SVDQ_FMT_INT) {
-    // the 512-thread block reduces the per-block maxima in two 256-thread halves
     float a = 0.f;
-    for (int q = threadIdx.x; q < p.n_amax; q += 512) a = fmaxf(a, p.amax_part[q]);
+    for (int q = threadIdx.x; q < p.n_amax; q += 64 * NW) a = fmaxf(a, p.amax_part[q]);
     a = wave_max(a);
     __shared__ float shw[NW];
-    if (lane == 0) shw[wave] = a;
+    if (L.lane == 0) shw[wave] = a;
     __syncthreads();
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < NW; q++) amax = fmaxf(amax, shw[q]);
-    qmax = (float)((1 << (p.bits - 1)) - 1);
-    sx = amax / qmax;
-    ysx = (sx >= 0x1p-90f && sx <= 0x1p90f) ? 1.0f / sx : 0.f;
-    if (p.sx_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *p.sx_out = sx;
+    L.qmax = (float)((1 << (p.bits - 1)) - 1);
+    L.sx = amax / L.qmax;
+    L.ysx = (L.sx >= 0x1p-90f && L.sx <= 0x1p90f) ? 1.0f / L.sx : 0.f;
+    if (p.sx_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *p.sx_out = L.sx;
   }
-  (void)sh;
 
   v4f acc[ACT_RCHUNK / 16];
 #pragma unroll
   for (int n = 0; n < ACT_RCHUNK / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = kbeg + 128 * wave; k0 < kend; k0 += 128 * NW) {
-    const int k = k0 + 32 * g;
-    constexpr int RW = DT::is_bf16 ? 16 : 32;
-    u32 raw[RW];
-    load_row32<DT>(xrow, k, p.M, p.x_vec_ok, raw);
-    // X^ = D(x / scale) in chunks of 8; xb: X^ as stored (bf16 pairs or f32 bits)
-    u32 xb[RW];
-    float amax = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      float s8[8], y8[8];
-      load8(p.scale, k + 8 * c, p.M, 1.f, s8);
-      if (p.recip)
-        load8(p.recip, k + 8 * c, p.M, 1.f, y8);
-      else
-#pragma unroll
-        for (int j = 0; j < 8; j++) y8[j] = 0.f;
-#pragma unroll
-      for (int h = 0; h < 4; h++) {
-        const int j = 8 * c + 2 * h;
-        if constexpr (DT::is_bf16) {
-          const u32 w = raw[j / 2];
-          const float q0 = div_rn(__uint_as_float(w << 16), s8[2 * h], y8[2 * h]);
-          const float q1 = div_rn(__uint_as_float(w & 0xFFFF0000u), s8[2 * h + 1], y8[2 * h + 1]);
-          typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-          typedef float f2 __attribute__((ext_vector_type(2)));
-          const u32 pk = __builtin_bit_cast(u32, __builtin_convertvector(f2{q0, q1}, bf2));
-          xb[j / 2] = pk;
-          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(pk << 16)), fabsf(__uint_as_float(pk & 0xFFFF0000u))));
-        } else {
-          const float q0 = div_rn(__uint_as_float(raw[j]), s8[2 * h], y8[2 * h]);
-          const float q1 = div_rn(__uint_as_float(raw[j + 1]), s8[2 * h + 1], y8[2 * h + 1]);
-          xb[j] = __float_as_uint(q0);
-          xb[j + 1] = __float_as_uint(q1);
-          amax = fmaxf(amax, fmaxf(fabsf(q0), fabsf(q1)));
-        }
-      }
-    }
-    auto val = [&](int j) -> float {
-      if constexpr (DT::is_bf16)
-        return (j & 1) ? __uint_as_float(xb[j / 2] & 0xFFFF0000u) : __uint_as_float(xb[j / 2] << 16);
-      else
-        return __uint_as_float(xb[j]);
-    };
-    if (do_codes && b < p.B) {
-      if constexpr (FMT == SVDQ_FMT_MX) {
-        const int e = mx_exponent(amax);
-        const float sc = pow2f(e);
-        u32 w4[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          float v[8];
-#pragma unroll
-          for (int h = 0; h < 8; h++) v[h] = val(8 * q + h);
-          w4[q] = fp4_pack8(v, sc);
-        }
-        *reinterpret_cast<uint4*>(p.codes + (int64_t)b * p.ldc + k / 2) = uint4{w4[0], w4[1], w4[2], w4[3]};
-        const int64_t si = p.mxs_tiled ? mx_scale_tiled_index(b, k / 32, p.Kp / 128) : (int64_t)b * p.lds + k / 32;
-        p.mxs[si] = (uint8_t)(e + 127);
-      } else if constexpr (NIB) {
-        u32 ws[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          u32 r = 0;
-#pragma unroll
-          for (int h = 0; h < 8; h++) {
-            const float z = val(8 * q + h);
-            const int c = sx == 0.f ? 0 : (int)fminf(fmaxf(__builtin_rintf(div_rn(z, sx, ysx)), -qmax), qmax);
-            r |= (u32)(c & 0xF) << (4 * h);
-          }
-          ws[q] = r;
-        }
-        *reinterpret_cast<uint4*>(p.codes + (int64_t)b * p.ldc + k / 2) = uint4{ws[0], ws[1], ws[2], ws[3]};
-      } else {
-        u32 ws[8];
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-          u32 r = 0;
-#pragma unroll
-          for (int h = 0; h < 4; h++) {
-            const float z = val(4 * q + h);
-            const int c = sx == 0.f ? 0 : (int)fminf(fmaxf(__builtin_rintf(div_rn(z, sx, ysx)), -qmax), qmax);
-            r |= (u32)(c & 0xFF) << (8 * h);
-          }
-          ws[q] = r;
-        }
-        uint4* dst = reinterpret_cast<uint4*>(p.codes + (int64_t)b * p.ldc + k);
-        dst[0] = uint4{ws[0], ws[1], ws[2], ws[3]};
-        dst[1] = uint4{ws[4], ws[5], ws[6], ws[7]};
-      }
-    }
-    if (nbl > 0) {
-      if constexpr (DT::is_bf16) {
-        v4i bw[ACT_RCHUNK / 16][4];
-#pragma unroll
-        for (int n = 0; n < ACT_RCHUNK / 16; n++)
-          if (n < nbl) {
-            const T* tile = l1t + ((int64_t)(rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + lane * 8;
-#pragma unroll
-            for (int s = 0; s < 4; s++) bw[n][s] = *reinterpret_cast<const v4i*>(tile + s * 512);
-          }
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-          const v8bf av = __builtin_bit_cast(v8bf, v4i{(int)xb[4 * s], (int)xb[4 * s + 1], (int)xb[4 * s + 2], (int)xb[4 * s + 3]});
-#pragma unroll
-          for (int n = 0; n < ACT_RCHUNK / 16; n++)
-            if (n < nbl) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, bw[n][s]), acc[n], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < ACT_RCHUNK / 16; n++) {
-          if (n < nbl) {
-            const float* tile = reinterpret_cast<const float*>(l1t) +
-                                ((int64_t)(rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + lane * 4;
-#pragma unroll
-            for (int c = 0; c < 8; c++) {
-              const float4 lr = *reinterpret_cast<const float4*>(tile + c * 256);
-              const float l4[4] = {lr.x, lr.y, lr.z, lr.w};
-#pragma unroll
-              for (int e = 0; e < 4; e++)
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xb[4 * c + e]), l4[e], acc[n], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-  }
+  // full steps first (k0 ascending), then the tail and padding
+  const int kfull = p.x_vec_ok ? p.M : 0;
+  int k0 = kbeg + 128 * wave;
+  for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc);
+  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false>(p, xrow, L, k0, acc);
 
-  if (nbl > 0) {
+  if (L.nbl > 0) {
     // fixed-order sum of the waves' partial down-projections
 #pragma unroll
     for (int n = 0; n < ACT_RCHUNK / 16; n++)
-      if (n < nbl)
+      if (n < L.nbl)
 #pragma unroll
-        for (int v = 0; v < 4; v++) red[wave][4 * g + v][16 * n + i] = acc[n][v];
+        for (int v = 0; v < 4; v++) red[wave][4 * L.g + v][16 * n + L.i] = acc[n][v];
     __syncthreads();
-    const int ncols = nbl * 16;
+    const int ncols = L.nbl * 16;
     for (int idx = threadIdx.x; idx < 16 * ncols; idx += 64 * NW) {
       const int r = idx / ncols, c = idx - r * ncols;
       float s = 0.f;
@@ -381,11 +457,20 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
       const int bb = row0 + r;
       if (bb < p.B) {
         if (p.k_chunks == 1)
-          reinterpret_cast<T*>(p.down)[(int64_t)bb * p.rp + rbase + c] = DT::from_f32(s);
+          reinterpret_cast<T*>(p.down)[(int64_t)bb * p.rp + L.rbase + c] = DT::from_f32(s);
         else
-          p.down_part[((int64_t)blockIdx.y * p.B + bb) * p.rp + rbase + c] = s;
+          p.down_part[((int64_t)blockIdx.y * p.B + bb) * p.rp + L.rbase + c] = s;
       }
     }
+  }
+}
+
+// recip[m] = RN(1 / scale[m]) (IEEE division), or 0 outside [2^-90, 2^90].
+__global__ void k_reciprocals(const float* __restrict__ scale, int M, float* __restrict__ recip) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m < M) {
+    const float s = scale[m];
+    recip[m] = (s >= 0x1p-90f && s <= 0x1p90f) ? 1.0f / s : 0.f;
   }
 }
 
@@ -481,25 +566,33 @@ hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t 
   return hipGetLastError();
 }
 
+hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream_t stream) {
+  k_reciprocals<<<(M + 255) / 256, 256, 0, stream>>>(scale, M, recip);
+  return hipGetLastError();
+}
+
 hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream) {
   const dim3 grid(row_blocks, p.k_chunks, r_chunks);
   const int threads = 64 * ACT_WAVES;
   const bool nib = fmt == SVDQ_FMT_MX || p.bits <= 4;
+#define SVDQ_ACT(DT, FMT, NIB) k_act_quant<DT, FMT, NIB><<<grid, threads, 0, stream>>>(p)
+  if (!p.recip) return hipErrorInvalidValue;
   if (dtype == SVDQ_BF16) {
     if (fmt == SVDQ_FMT_MX)
-      k_act_quant<BF16, SVDQ_FMT_MX, true><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(BF16, SVDQ_FMT_MX, true);
     else if (nib)
-      k_act_quant<BF16, SVDQ_FMT_INT, true><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(BF16, SVDQ_FMT_INT, true);
     else
-      k_act_quant<BF16, SVDQ_FMT_INT, false><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(BF16, SVDQ_FMT_INT, false);
   } else {
     if (fmt == SVDQ_FMT_MX)
-      k_act_quant<F32, SVDQ_FMT_MX, true><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(F32, SVDQ_FMT_MX, true);
     else if (nib)
-      k_act_quant<F32, SVDQ_FMT_INT, true><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(F32, SVDQ_FMT_INT, true);
     else
-      k_act_quant<F32, SVDQ_FMT_INT, false><<<grid, threads, 0, stream>>>(p);
+      SVDQ_ACT(F32, SVDQ_FMT_INT, false);
   }
+#undef SVDQ_ACT
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ struct ActParams {
   int64_t ldx;
   int B, M, Kp;
   const float* scale;
-  const float* recip;  // RN(1/scale) (0 = use IEEE division), or NULL for IEEE division everywhere
+  const float* recip;  // RN(1/scale), 0 where the scale lies outside [2^-90, 2^90]
   uint8_t* codes;  // [B][ldc] bytes, or NULL (down-projection only)
   int64_t ldc;
   uint8_t* mxs;  // MX scales: row-major [B][lds], or stage-tiled when mxs_tiled
@@ -62,6 +62,8 @@ hipError_t launch_amax(const void* z, int64_t rows, int64_t cols, int64_t szr, i
                        int dtype, float* part, int nparts, hipStream_t stream);
 hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t szr, int64_t szc, int dtype, int bits,
                              const float* part, int nparts, void* out, int64_t ldo, float* s_out, hipStream_t stream);
+// recip[m] = RN(1 / scale[m]) for scale[m] in [2^-90, 2^90], else 0 (the prepared RECIP section).
+hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream_t stream);
 hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream);
 hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, void* down, int dtype,
                               hipStream_t stream);

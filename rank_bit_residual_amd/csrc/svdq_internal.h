@@ -47,7 +47,7 @@ inline Dims make_dims(int64_t M, int64_t N, int64_t rank, int fmt, int bits, int
 void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]);
 
 // Workspace sections of svdq_linear.
-enum { WS_CODES = 0, WS_SCALES, WS_DOWN, WS_PARTIAL, WS_AMAX, WS_SX, WS_END, WS_NSEC };
+enum { WS_CODES = 0, WS_SCALES, WS_DOWN, WS_PARTIAL, WS_AMAX, WS_SX, WS_RECIP, WS_END, WS_NSEC };
 struct LaunchPlan {
   int64_t B;
   int row_blocks;   // activation row blocks of kernel (a) (16 rows each)

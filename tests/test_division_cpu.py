@@ -7,6 +7,12 @@ quotient, an input or the scale leaves [2^-90, 2^90]. That claim ("equals the co
 rounded quotient") is tested here against the C library's IEEE float division for every
 positive finite bfloat16 x and every smoothing scale of the five workloads, plus random
 binary32 inputs. gcc's fmaf is correctly rounded, like the GPU's v_fma_f32.
+
+The bf16 kernels take a cheaper route that is checked the same way: t = RN(x * RN(1/s)),
+then RN_bf16(t), except where t lies within 8 ulps of a bf16 rounding midpoint or is not a
+normal number while x is nonzero (then the correctly rounded division above). The INT
+codes use rint(RN(z * RN(1/s_x))) unless that product lies within 2^-14 of a half-integer.
+Both must reproduce the plain definition (IEEE division, then rounding) exactly.
 """
 import os
 import subprocess
@@ -36,7 +42,66 @@ static float div_rn(float x, float s, float y) {
 static float recip(float s) { return (s >= 0x1p-90f && s <= 0x1p90f) ? 1.0f / s : 0.0f; }
 static uint64_t st = 88172645463325252ull;
 static uint32_t rnd(void) { st ^= st << 13; st ^= st >> 7; st ^= st << 17; return (uint32_t)st; }
+static float bf16_round(float v) {  /* RNE to bfloat16, finite v */
+  uint32_t u; memcpy(&u, &v, 4); u += 0x7FFFu + ((u >> 16) & 1u); u &= 0xFFFF0000u; memcpy(&v, &u, 4); return v;
+}
+static int risky(float t, float x) {
+  uint32_t u; memcpy(&u, &t, 4);
+  int near_mid = ((u + 8u) & 0xFFF0u) == 0x8000u;
+  int not_normal = fpclassify(t) != FP_NORMAL && x != 0.0f;
+  return near_mid || not_normal;
+}
+static float smooth_bf16_fast(float x, float s, float y) {
+  float t = x * y;
+  if (risky(t, x)) t = div_rn(x, s, y);
+  return bf16_round(t);
+}
+static int int_code_fast(float z, float sx, float ysx, float qmax) {
+  float d = z * ysx;
+  if (fabsf(d - rintf(d)) >= 0.5f - 0x1p-14f) d = div_rn(z, sx, ysx);
+  return (int)fminf(fmaxf(rintf(d), -qmax), qmax);
+}
+static int int_code_ref(float z, float sx, float qmax) { return (int)fminf(fmaxf(rintf(z / sx), -qmax), qmax); }
 int main(int argc, char** argv) {
+  if (argc > 2) {                          /* fast bf16 smoothing and INT codes */
+    FILE* f = fopen(argv[1], "rb");
+    fseek(f, 0, SEEK_END); long n = ftell(f) / 4; fseek(f, 0, SEEK_SET);
+    float* sc = malloc(n * 4); if (fread(sc, 4, n, f) != (size_t)n) return 2; fclose(f);
+    long bad = 0, total = 0, slow = 0, typical = 0;
+    for (long i = 0; i < n; i++) {
+      float s = sc[i], y = recip(s);
+      for (uint32_t h = 0; h < 0x7F80; h++) {
+        uint32_t u = h << 16; float x; memcpy(&x, &u, 4);
+        for (int sg = 0; sg < 2; sg++, x = -x) {
+          float a = smooth_bf16_fast(x, s, y), b = bf16_round(x / s);
+          if (memcmp(&a, &b, 4)) { if (bad < 5) printf("bad smooth x=%a s=%a got %a want %a\n", x, s, a, b); bad++; }
+          if (y != 0.0f && fabsf(x) >= 0x1p-30f && fabsf(x) <= 0x1p30f) { slow += risky(x * y, x); typical++; }
+          total++;
+        }
+      }
+    }
+    /* INT: s_x = RN(amax / qmax) for amax = every 97th positive bf16, z = every bf16 with |z| <= amax */
+    long ibad = 0, itotal = 0;
+    for (int bits = 2; bits <= 8; bits += 2) {
+      float qmax = (float)((1 << (bits - 1)) - 1);
+      for (uint32_t ha = 0x0080; ha < 0x7F80; ha += 97) {
+        uint32_t ua = ha << 16; float amax; memcpy(&amax, &ua, 4);
+        float sx = amax / qmax, ysx = recip(sx);
+        if (ysx == 0.0f) continue;
+        for (uint32_t hz = 0; hz <= ha; hz += (ha > 0x4000 ? 3 : 1)) {
+          uint32_t uz = hz << 16; float z; memcpy(&z, &uz, 4);
+          for (int sg = 0; sg < 2; sg++, z = -z) {
+            if (int_code_fast(z, sx, ysx, qmax) != int_code_ref(z, sx, qmax)) {
+              if (ibad < 5) printf("bad int z=%a sx=%a\n", z, sx); ibad++;
+            }
+            itotal++;
+          }
+        }
+      }
+    }
+    printf("%ld %ld %ld %ld %ld %ld\n", bad, total, slow, typical, ibad, itotal);
+    return 0;
+  }
   FILE* f = fopen(argv[1], "rb");
   fseek(f, 0, SEEK_END); long n = ftell(f) / 4; fseek(f, 0, SEEK_SET);
   float* sc = malloc(n * 4); if (fread(sc, 4, n, f) != (size_t)n) return 2; fclose(f);
@@ -79,3 +144,24 @@ def test_fast_division_matches_ieee_division():
     bad, total = map(int, out.strip().splitlines()[-1].split())
     assert total > 5e8
     assert bad == 0, out
+
+
+def test_fast_bf16_smoothing_and_int_codes_match_definition():
+    rng = np.random.default_rng(1)
+    wl_scales = np.unique(np.concatenate([make_inputs(cid, B=min(WORKLOADS[cid].B, 64))[2] for cid in WORKLOADS]))
+    picks = [rng.choice(wl_scales, 600, replace=False),
+             np.ldexp(rng.random(600) + 0.5, rng.integers(-100, 101, 600)).astype(np.float32),
+             np.array([2.0**-90, 2.0**90, 2.0**-91, 2.0**91, 2.0**-120, 2.0**120, 1.0, 3.0, 0.1, 7.0,
+                       float.fromhex("0x1.fffffep-91"), float.fromhex("0x1.000002p90")], np.float32)]
+    allsc = np.unique(np.concatenate(picks).astype(np.float32))
+    with tempfile.TemporaryDirectory() as d:
+        src, exe, dat = os.path.join(d, "t.c"), os.path.join(d, "t"), os.path.join(d, "s.bin")
+        open(src, "w").write(C_SRC)
+        allsc.tofile(dat)
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", src, "-o", exe, "-lm"], check=True)
+        out = subprocess.run([exe, dat, "fast"], capture_output=True, text=True, check=True, timeout=900).stdout
+    bad, total, slow, typical, ibad, itotal = map(int, out.strip().splitlines()[-1].split())
+    assert total > 5e7 and itotal > 1e7
+    assert bad == 0 and ibad == 0, out
+    # the correction is rare for ordinary magnitudes (about 17 in 65536 products)
+    assert slow < typical * 5e-4, out

@@ -15,6 +15,8 @@ import rank_bit_residual_amd as R
 from oracle import svdquant as O
 from workloads import WORKLOADS, make_inputs
 
+from cases import double_boundary_case
+
 pytestmark = pytest.mark.gpu
 
 TD = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -54,6 +56,26 @@ def test_smooth_inputs_bit_exact(dtype):
     xt = _g(x.T.copy(), dtype).t()
     xs2, _ = R.smooth_inputs(xt, _g(w, dtype), torch.from_numpy(s).to(dev()))
     assert torch.equal(xs2, xs)
+
+
+def test_smooth_bf16_every_value():
+    """Every finite bf16 x (both signs) against 64 scales: workload-like values, powers of
+    two, values whose reciprocal is inexact, and scales outside [2^-90, 2^90]."""
+    rng = np.random.default_rng(15)
+    h = np.arange(0, 0x7F80, dtype=np.uint32)
+    xv = np.concatenate([h, h | 0x8000]).astype(np.uint32) << 16
+    x = xv.view(np.float32)[:, None] * np.ones((1, 64), np.float32)
+    s = np.concatenate([
+        np.abs(rng.standard_normal(40)) * 3 + 0.01,
+        [1.0, 2.0, 0.5, 3.0, 0.1, 7.0, 1e-3, 1e3, 2.0**-90, 2.0**90, 2.0**-91, 2.0**91, 2.0**-120, 2.0**120],
+        np.ldexp(rng.random(10) + 0.5, rng.integers(-89, 90, 10)),
+    ]).astype(np.float32)
+    w = np.ones((64, 3), np.float32)
+    xs, _ = R.smooth_inputs(_g(x, "bf16"), _g(w, "bf16"), torch.from_numpy(s).to(dev()))
+    want = O.smooth_activations(x, s, "bf16")
+    got = _np(xs)
+    bad = np.argwhere(_bits(got) != _bits(want))
+    assert bad.size == 0, f"{len(bad)} mismatches, first x={x[tuple(bad[0])]!r} s={s[bad[0][1]]!r}"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -104,6 +126,12 @@ def test_activation_codes_bit_exact_workloads(cid):
     wl = WORKLOADS[cid]
     x, w, s = make_inputs(cid)
     _check_codes(x, s, wl.fmt, wl.bits, wl.dtype)
+
+
+def test_activation_codes_double_rounding_boundaries():
+    x, s = double_boundary_case()
+    _check_codes(x, s, "mx", 4, "bf16")
+    _check_codes(x, s, "int", 8, "bf16")
 
 
 @pytest.mark.parametrize("fmt,bits,dtype", [("mx", 4, "bf16"), ("mx", 4, "f32"), ("int", 4, "bf16"), ("int", 3, "f32"),
