@@ -30,7 +30,16 @@ sys.path.insert(0, ROOT)
 METRIC = "svdquant_linear TFLOP/s (2BMN) and % of MFMA/HBM roofline, 1×MI355X"
 # MI355X published dense peaks
 PEAK = {"hbm": 8000.0, "mxfp4": 10100.0, "int8": 5000.0, "bf16": 2500.0, "fp32": 157.3}
-GEMM_SRC = os.path.join(ROOT, "rank_bit_residual_amd", "csrc", "k_gemm.hip")
+CSRC = os.path.join(ROOT, "rank_bit_residual_amd", "csrc")
+
+
+def gemm_kernel(wl, B):
+    """(kernel name, source file) of the residual GEMM that svdq_linear launches for this shape."""
+    if wl.fmt == "mx" and wl.dtype == "bf16" and B <= 64:
+        return "k_gemm_decode_mx", os.path.join(CSRC, "k_gemm_decode.hip")
+    if wl.fmt == "mx" and wl.dtype == "bf16" and B >= 256:
+        return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
+    return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 
 
 def algorithmic(wl, B):
@@ -51,15 +60,16 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(workload_name):
+def pmc_traffic(wl, B):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"k_gemm_{workload_name}_pmc.json")
+    kname, src = gemm_kernel(wl, B)
+    path = os.path.join(ROOT, "profiles", f"{kname}_{wl.name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha") != source_sha(GEMM_SRC):
+    if d.get("source_sha") != source_sha(src):
         return None
     return d.get("hbm_bytes_per_dispatch")
 
@@ -138,24 +148,33 @@ def run(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # ---- timed region: eager launches
+    def stage_times(steps):
+        ms = (ctypes.c_float * (steps * L.NSTAGES))()
+        n = ctypes.c_int()
+        L.check(lib.svdq_profile_end(ms, steps, ctypes.byref(n)))
+        per = np.array(ms[: n.value * L.NSTAGES], dtype=np.float64).reshape(n.value, L.NSTAGES)
+        return {name: float(per[:, k].mean()) for k, name in enumerate(L.STAGE_NAMES) if per[:, k].any()}
+
+    # ---- timed region: eager launches. The library records one HIP event pair around its
+    # residual-GEMM launch on the call's stream (stage 3 only, to keep host overhead low), so
+    # the roofline's kernel duration comes from the timed calls themselves.
+    GEMM_STAGE = 3
+    L.check(lib.svdq_profile_begin(args.steps, 1 << GEMM_STAGE))
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t_eager = time.perf_counter() - t0
+    gemm_ms = stage_times(args.steps)["gemm"]
     work = algorithmic(wl, B)
     value = work["flops"] * args.steps / t_eager / 1e12
 
-    # ---- per-kernel HIP-event timing (events recorded by the library around each launch)
-    L.check(lib.svdq_profile_begin(args.steps))
+    # ---- per-kernel breakdown of every stage (separate pass; informational)
+    L.check(lib.svdq_profile_begin(args.steps, (1 << L.NSTAGES) - 1))
     for i in range(args.steps):
         step(i)
-    ms = (ctypes.c_float * (args.steps * L.NSTAGES))()
-    n = ctypes.c_int()
-    L.check(lib.svdq_profile_end(ms, args.steps, ctypes.byref(n)))
-    per = np.array(ms[: n.value * L.NSTAGES], dtype=np.float64).reshape(n.value, L.NSTAGES)
-    stage_ms = {name: float(per[:, k].mean()) for k, name in enumerate(L.STAGE_NAMES) if per[:, k].any()}
+    stage_ms = stage_times(args.steps)
 
     # ---- HIP-graph replay of the same calls (reported separately, not the headline)
     graph = None
@@ -185,11 +204,11 @@ def run(args):
                  "value": work["flops"] * reps * per_graph / t_graph / 1e12, "calls_per_graph": per_graph}
 
     # ---- roofline of the dominant kernel (the residual GEMM)
-    gemm_s = stage_ms["gemm"] / 1e3
+    gemm_s = gemm_ms / 1e3
     mfma_peak = PEAK["mxfp4"] if wl.fmt == "mx" else PEAK["int8"]
     t_mfma = work["flops"] / (mfma_peak * 1e12)
     t_hbm = work["gemm_bytes"] / (PEAK["hbm"] * 1e9)
-    traffic = pmc_traffic(wl.name)
+    traffic = pmc_traffic(wl, B)
     if t_mfma >= t_hbm:
         ach = work["flops"] / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak}
@@ -197,8 +216,8 @@ def run(args):
         ach = work["gemm_bytes"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]}
     roof["traffic"] = traffic
-    roof["kernel"] = "k_gemm"
-    roof["avg_ms"] = stage_ms["gemm"]
+    roof["kernel"] = gemm_kernel(wl, B)[0]
+    roof["avg_ms"] = gemm_ms
     roof["algorithmic_bytes"] = work["gemm_bytes"]
 
     out = {
@@ -218,8 +237,10 @@ def run(args):
     print(json.dumps(out), flush=True)
 
 
-def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, workload, command):
-    """Per-dispatch HBM bytes of k_gemm from rocprofv3 counter CSVs, scaled by a copy kernel."""
+def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, wl, command):
+    """Per-dispatch HBM bytes of the residual GEMM from rocprofv3 counter CSVs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain
+    device copy of copy_bytes bytes."""
     import csv
 
     def per_dispatch(path, counter, name_pred):
@@ -230,15 +251,16 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, worklo
                     vals.append(float(row["Counter_Value"]))
         return sum(vals) / len(vals) if vals else float("nan"), len(vals)
 
-    is_gemm = lambda k: "k_gemm" in k  # noqa: E731
-    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    kname, src = gemm_kernel(wl, wl.B)
+    is_gemm = lambda k: (kname + "<") in k or (kname + "(") in k  # noqa: E731
+    is_copy = lambda k: "copyBuffer" in k  # the runtime's device-to-device copy kernel  # noqa: E731
     f_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE", is_gemm)
     w_kib, nw = per_dispatch(write_csv, "WRITE_SIZE", is_gemm)
     cf_kib, _ = per_dispatch(cfetch_csv, "FETCH_SIZE", is_copy)
     cw_kib, _ = per_dispatch(cwrite_csv, "WRITE_SIZE", is_copy)
     rf = copy_bytes / (cf_kib * 1024)
     rw = copy_bytes / (cw_kib * 1024)
-    d = {"kernel": "k_gemm", "workload": workload, "source_sha": source_sha(GEMM_SRC),
+    d = {"kernel": kname, "workload": wl.name, "source_sha": source_sha(src),
          "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
          "copy_factor_fetch": rf, "copy_factor_write": rw,
          "hbm_bytes_per_dispatch": f_kib * 1024 * rf + w_kib * 1024 * rw, "command": command}
@@ -258,12 +280,24 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_BYTES"))
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--copy-probe", type=int, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.pmc_summary:
         from workloads import WORKLOADS
 
         f, w_, cf, cw, cb = args.pmc_summary
-        pmc_summary(f, w_, cf, cw, float(cb), WORKLOADS[args.workload].name, args.pmc_command)
+        pmc_summary(f, w_, cf, cw, float(cb), WORKLOADS[args.workload], args.pmc_command)
+        return 0
+    if args.copy_probe:
+        import torch
+
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_probe} bytes 5 times", flush=True)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures the operator on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)

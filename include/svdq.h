@@ -227,17 +227,20 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
 /* --------------------------------------------------------------------------------------
  * Kernel timing (profiling aid; not on any page). Between svdq_profile_begin and
  * svdq_profile_end, each svdq_linear call records a HIP event pair around every kernel it
- * launches, on the call's stream, for up to max_calls calls. Stages: 0 = per-tensor max
- * pre-pass (INT), 1 = smooth+quantise+down-projection, 2 = split-K down reduction,
- * 3 = residual GEMM + epilogue; a stage that did not run reads 0.
+ * launches whose stage bit is set in stage_mask, on the call's stream, for up to max_calls
+ * calls. Stages: 0 = per-tensor max pre-pass (INT), 1 = smooth+quantise+down-projection,
+ * 2 = split-K down reduction, 3 = residual GEMM + epilogue; a stage that did not run or was
+ * not selected reads 0. Each event pair costs host time per call, so a throughput
+ * measurement should select only the stages it needs.
  *   svdq_profile_begin: creates the events (host call; no device memory). EINVAL if
- *     max_calls < 1 or a session is already open; EHIP if event creation fails.
+ *     max_calls < 1, stage_mask selects no stage or a bit above 3, or a session is already
+ *     open; EHIP if event creation fails.
  *   svdq_profile_end: waits for the recorded events, writes ms[call * SVDQ_NSTAGES + stage]
  *     for the n_calls (<= cap) calls recorded, destroys the events and closes the session.
  * Not thread-safe: one session per process at a time.
  * ------------------------------------------------------------------------------------ */
 #define SVDQ_NSTAGES 4
-int svdq_profile_begin(int max_calls);
+int svdq_profile_begin(int max_calls, unsigned stage_mask);
 int svdq_profile_end(float* ms, int cap, int* n_calls);
 
 #ifdef __cplusplus

@@ -56,6 +56,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 struct Profile {
   bool open = false;
   int max_calls = 0, calls = 0;
+  unsigned mask = 0;              // stages that record events
   std::vector<hipEvent_t> ev;     // [call][stage][begin, end]
   std::vector<uint8_t> recorded;  // [call][stage]: both events of the pair were recorded
 };
@@ -68,11 +69,12 @@ struct StageTimer {
     if (g_prof.open && g_prof.calls < g_prof.max_calls) call = g_prof.calls++;
   }
   hipEvent_t ev(int stage, int which) const { return g_prof.ev[((size_t)call * SVDQ_NSTAGES + stage) * 2 + which]; }
+  bool on(int stage) const { return call >= 0 && ((g_prof.mask >> stage) & 1u); }
   void begin(int stage) const {
-    if (call >= 0) hipEventRecord(ev(stage, 0), s);
+    if (on(stage)) hipEventRecord(ev(stage, 0), s);
   }
   void end(int stage) const {
-    if (call >= 0 && hipEventRecord(ev(stage, 1), s) == hipSuccess)
+    if (on(stage) && hipEventRecord(ev(stage, 1), s) == hipSuccess)
       g_prof.recorded[(size_t)call * SVDQ_NSTAGES + stage] = 1;
   }
 };
@@ -325,9 +327,10 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   return st;
 }
 
-int svdq_profile_begin(int max_calls) {
+int svdq_profile_begin(int max_calls, unsigned stage_mask) {
   clear_error();
   if (max_calls < 1) return set_error(SVDQ_EINVAL, "max_calls must be >= 1");
+  if (stage_mask == 0 || (stage_mask >> SVDQ_NSTAGES)) return set_error(SVDQ_EINVAL, "stage_mask must select stages 0..3");
   if (g_prof.open) return set_error(SVDQ_EINVAL, "a profiling session is already open");
   g_prof.ev.assign((size_t)max_calls * SVDQ_NSTAGES * 2, nullptr);
   for (auto& e : g_prof.ev) {
@@ -341,6 +344,7 @@ int svdq_profile_begin(int max_calls) {
   }
   g_prof.recorded.assign((size_t)max_calls * SVDQ_NSTAGES, 0);
   g_prof.open = true;
+  g_prof.mask = stage_mask;
   g_prof.max_calls = max_calls;
   g_prof.calls = 0;
   return SVDQ_OK;

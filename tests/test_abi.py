@@ -47,3 +47,10 @@ def test_host_calls_report_errors_without_a_gpu():
     ws = ctypes.c_size_t()
     assert lib.svdq_workspace_bytes(16, 64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F32, ctypes.byref(ws)) == 0
     assert ws.value > 0
+    # profiling session: argument errors are reported before any HIP call
+    assert lib.svdq_profile_begin(0, 8) == _lib.SVDQ_EINVAL
+    assert lib.svdq_profile_begin(4, 0) == _lib.SVDQ_EINVAL
+    assert lib.svdq_profile_begin(4, 16) == _lib.SVDQ_EINVAL
+    assert b"stage_mask" in lib.svdq_last_error()
+    n = ctypes.c_int()
+    assert lib.svdq_profile_end(None, 0, ctypes.byref(n)) == _lib.SVDQ_EINVAL  # no open session
