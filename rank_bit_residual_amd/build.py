@@ -27,6 +27,7 @@ HIP_SOURCES = {
     "k_gemm.hip": [],
     "k_gemm_mx.hip": [],
     "k_gemm_decode.hip": [],
+    "k_gemm_int.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

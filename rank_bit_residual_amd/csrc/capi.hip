@@ -321,6 +321,10 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
     ge = B <= 64 ? launch_gemm_mx_decode(g, dtype, s) : launch_gemm_mx_large(g, dtype, s);
     if (ge == hipErrorNotSupported) g.kstages = (int)(d.code_row_bytes() / 128);
   }
+  if (fmt == SVDQ_FMT_INT) {
+    g.kstages = (int)(d.code_row_bytes() / 128);  // 128-byte stages (256 codes)
+    ge = launch_gemm_int4(g, bits, dtype, s);
+  }
   if (ge == hipErrorNotSupported) ge = launch_gemm(g, fmt, bits, dtype, s);
   st = hip_status(ge, "residual GEMM launch");
   tm.end(3);

@@ -1,0 +1,43 @@
+// Pieces shared by the LDS-ring GEMM kernels: the LDS address space pointer type for
+// direct global->LDS loads, and waits on the vector-memory counter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace svdq {
+namespace dev {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(n) for a compile-time n (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until the stage about to be read has landed: remaining_after = number of later
+// stages already issued (0 .. NS-2), LPS = loads per stage per wave. Loads complete in
+// issue order, so allowing LPS * remaining_after outstanding leaves the wanted stage done.
+template <int LPS, int NS>
+__device__ inline void wait_stage(int remaining_after) {
+  if constexpr (NS >= 5) {
+    if (remaining_after >= 3) {
+      wait_vmcnt<LPS * 3>();
+      return;
+    }
+  }
+  if constexpr (NS >= 4) {
+    if (remaining_after >= 2) {
+      wait_vmcnt<LPS * 2>();
+      return;
+    }
+  }
+  if (remaining_after >= 1)
+    wait_vmcnt<LPS * 1>();
+  else
+    wait_vmcnt<0>();
+}
+
+}  // namespace dev
+}  // namespace svdq

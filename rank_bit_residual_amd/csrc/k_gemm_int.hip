@@ -1,0 +1,223 @@
+// Residual GEMM for per-tensor INT codes of up to 4 bits on gfx950 (step (c) of the operator):
+//   Y = D( s_x s_R (Q(X^) Q(R)) + down L2 )
+// with exact integer products on v_mfma_i32_32x32x32_i8 and the up-projection on bf16 (or
+// fp32) MFMAs into the dequantised fp32 accumulators.
+//
+// Pages: "SVDQuant Smoothing, Low-rank and Residual Quantization", "Formula and conventions"
+// item 3 (per-tensor INT quantisation; Y = (X^ L1) L2 + Q(X^) Q(R)); "flashinfer.gemm.
+// svdquant_linear" (the residual GEMM with the up-projection in its epilogue).
+//
+// Codes arrive as two's-complement nibbles (even k in the low nibble). The matrix cores take
+// int8, and a nibble c placed in the high half of a byte reads as the int8 16 c: per 32-bit
+// word, w & 0xF0F0F0F0 gives the odd codes and (w << 4) & 0xF0F0F0F0 the even ones, times 16.
+// Products are then 256 times the code products (|sum| <= 256 * 64 * K stays far below
+// 2^31 for K < 2^17) and the epilogue scales by 2^-8 exactly.
+//
+// Structure: a 64 x 64 output tile per 256-thread block, so that mid-size batches still give
+// hundreds of blocks. K advances in stages of 256 codes (128 bytes per row) that land in a
+// ring of LDS buffers through direct global->LDS loads, two stages ahead. Within a stage the
+// four waves split K: wave w takes the 16-byte chunks 2w and 2w+1 (two 32-code MFMA steps)
+// for the whole 64 x 64 tile, which keeps the nibble unpacking below the MFMA time. After
+// the K loop the four int32 partial tiles are summed through LDS (exact), and each wave
+// finishes one 32 x 32 quadrant: dequantise, up-projection, one rounding, masked store.
+// LDS rows are 128 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16-byte reads
+// of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
+#include "device_common.h"
+#include "gemm_pipe.h"
+#include "launch.h"
+#include "../../include/svdq.h"
+
+namespace svdq {
+namespace dev {
+
+namespace gi {
+constexpr int BM = 64, BN = 64;
+constexpr int SB = 128;                 // bytes per row per stage (256 codes)
+constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
+constexpr int STAGE = A_BYTES + B_BYTES;  // 16 KB
+constexpr int A_PER_WAVE = A_BYTES / 1024 / 4, B_PER_WAVE = B_BYTES / 1024 / 4;  // wave-wide 1 KB loads
+constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
+constexpr int NS = 4, DIST = 2;
+constexpr int SMEM = NS * STAGE;          // 64 KB; reused for the partial-tile exchange
+static_assert(4 * 4 * 16 * 64 * 4 <= SMEM, "partial tiles must fit the ring");
+}  // namespace gi
+
+__device__ inline int swz128(int row, int chunk) { return row * gi::SB + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Two words of nibble codes -> one MFMA operand of 16 int8 values (16 x code), in the order
+// (even codes of w0, odd of w0, even of w1, odd of w1); A and B use the same order.
+__device__ inline v4i nib16(u32 w0, u32 w1) {
+  return v4i{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u), (int)((w1 << 4) & 0xF0F0F0F0u),
+             (int)(w1 & 0xF0F0F0F0u)};
+}
+
+template <class DT>
+__global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
+  using namespace gi;
+  typedef typename DT::T T;
+  extern __shared__ __align__(1024) uint8_t smem[];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // ---- tile order: blocks i, i+8, ... share an XCD; within an XCD the row tiles of one
+  // column tile are consecutive, so a weight slice is fetched into that XCD's L2 once
+  const int tiles_m = (p.B + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int tid = blockIdx.x;
+  if ((ntiles & 7) == 0) tid = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int m0 = (tid % tiles_m) * BM, n0 = (tid / tiles_m) * BN;
+
+  // ---- per-lane DMA sources: wave-wide instruction u covers 8 rows x 128 bytes
+  const uint8_t* a_src[A_PER_WAVE];
+  const uint8_t* b_src[B_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < A_PER_WAVE; j++) {
+    const int q = (wave + 4 * j) * 64 + lane;
+    const int row = q >> 3, chunk = (q & 7) ^ ((row >> 1) & 7);
+    int gr = m0 + row;
+    gr = gr < p.B ? gr : p.B - 1;
+    a_src[j] = p.acodes + (int64_t)gr * p.lda + chunk * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < B_PER_WAVE; j++) {
+    const int q = (wave + 4 * j) * 64 + lane;
+    const int row = q >> 3, chunk = (q & 7) ^ ((row >> 1) & 7);
+    int gr = n0 + row;
+    gr = gr < p.npad ? gr : p.npad - 1;
+    b_src[j] = p.wcodes + (int64_t)gr * p.ldw + chunk * 16;
+  }
+  auto issue = [&](int st) {
+    uint8_t* base = smem + (st % NS) * STAGE;
+#pragma unroll
+    for (int j = 0; j < A_PER_WAVE; j++)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + st * SB), (lds_ptr_t)(base + (wave + 4 * j) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_PER_WAVE; j++)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + st * SB),
+                                       (lds_ptr_t)(base + A_BYTES + (wave + 4 * j) * 1024), 16, 0, 0);
+  };
+
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0;
+
+  const int nst = p.kstages;
+#pragma unroll
+  for (int s = 0; s < DIST; s++)
+    if (s < nst) issue(s);
+  const int ch = 2 * wave + g;  // this lane's 16-byte chunk of every stage
+  for (int s = 0; s < nst; s++) {
+    if (s + DIST < nst) issue(s + DIST);
+    const int ahead = nst - 1 - s;
+    wait_stage<LOADS_PER_STAGE, NS>(ahead < DIST ? ahead : DIST);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* base = smem + (s % NS) * STAGE;
+    v4i a4[2], b4[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) a4[i] = *reinterpret_cast<const v4i*>(base + swz128(32 * i + l32, ch));
+#pragma unroll
+    for (int j = 0; j < 2; j++) b4[j] = *reinterpret_cast<const v4i*>(base + A_BYTES + swz128(32 * j + l32, ch));
+#pragma unroll
+    for (int h = 0; h < 2; h++) {  // the chunk's two 16-code halves are two MFMA K steps
+      v4i av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) av[i] = nib16((u32)a4[i][2 * h], (u32)a4[i][2 * h + 1]);
+#pragma unroll
+      for (int j = 0; j < 2; j++) bv[j] = nib16((u32)b4[j][2 * h], (u32)b4[j][2 * h + 1]);
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- exact sum of the four waves' partial tiles: wave q then owns quadrant q = (i, j)
+  __syncthreads();
+  v4i* part = reinterpret_cast<v4i*>(smem);  // [wave][tile][v/4][lane] of 4 int32
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++)
+        part[((wave * 4 + 2 * i + j) * 4 + v4) * 64 + lane] =
+            v4i{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
+  __syncthreads();
+  const int qi = wave >> 1, qj = wave & 1;
+  v16f f;
+  const float scl = p.sx[0] * p.sr[0];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; v4++) {
+    v4i s = part[((0 * 4 + wave) * 4 + v4) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; w++) s += part[((w * 4 + wave) * 4 + v4) * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < 4; e++) f[4 * v4 + e] = ((float)s[e] * 0x1p-8f) * scl;
+  }
+
+  // ---- up-projection, rounding, masked store of quadrant (qi, qj)
+  const int row0 = m0 + 32 * qi, col = n0 + 32 * qj + l32;
+  if (p.rp > 0) {
+    const T* down = reinterpret_cast<const T*>(p.down);
+    const T* l2t = reinterpret_cast<const T*>(p.l2t);
+    int drow = row0 + l32;
+    drow = drow < p.B ? drow : p.B - 1;
+    const int bcol = col < p.npad ? col : p.npad - 1;
+    if constexpr (DT::is_bf16) {
+      for (int kk = 0; kk < p.rp; kk += 16) {
+        const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)drow * p.rp + kk + 8 * g));
+        const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + kk + 8 * g));
+        f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, f, 0, 0, 0);
+      }
+    } else {
+      for (int kk = 0; kk < p.rp; kk += 2) {
+        const float av = down[(int64_t)drow * p.rp + kk + g];
+        const float bv = l2t[(int64_t)bcol * p.rp + kk + g];
+        f = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, f, 0, 0, 0);
+      }
+    }
+  }
+  if (col < p.N) {
+    T* y = reinterpret_cast<T*>(p.y);
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const int row = row0 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (row < p.B) y[(int64_t)row * p.ldy + col] = DT::from_f32(f[v]);
+    }
+  }
+}
+
+}  // namespace dev
+
+using namespace dev;
+
+template <class DT>
+static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
+  const int tiles = ((p.B + gi::BM - 1) / gi::BM) * ((p.N + gi::BN - 1) / gi::BN);
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int4<DT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, gi::SMEM);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  k_gemm_int4<DT><<<tiles, 256, gi::SMEM, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Per-tensor INT with codes of at most 4 bits (nibbles); other formats fall back.
+hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
+  if (bits > 4 || p.kstages < 1) return hipErrorNotSupported;
+  if (dtype == SVDQ_BF16) return launch_int4_t<BF16>(p, stream);
+  return launch_int4_t<F32>(p, stream);
+}
+
+}  // namespace svdq

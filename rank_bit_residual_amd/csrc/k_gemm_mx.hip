@@ -18,12 +18,11 @@
 // the 16-byte reads of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
 #include "device_common.h"
 #include "launch.h"
+#include "gemm_pipe.h"
 #include "../../include/svdq.h"
 
 namespace svdq {
 namespace dev {
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int BM, int BN>
 struct MxCfg {
@@ -44,35 +43,6 @@ struct MxCfg {
 };
 
 __device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-// s_waitcnt vmcnt(n) for a compile-time n (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int LPS, int NS>
-__device__ inline void wait_stage(int remaining_after) {
-  // remaining_after = number of later stages already issued (0 .. NS-2); loads complete in
-  // issue order, so allowing LPS * remaining_after outstanding leaves the wanted stage done.
-  if constexpr (NS >= 5) {
-    if (remaining_after >= 3) {
-      wait_vmcnt<LPS * 3>();
-      return;
-    }
-  }
-  if constexpr (NS >= 4) {
-    if (remaining_after >= 2) {
-      wait_vmcnt<LPS * 2>();
-      return;
-    }
-  }
-  if (remaining_after >= 1)
-    wait_vmcnt<LPS * 1>();
-  else
-    wait_vmcnt<0>();
-}
 
 template <class DT, int BM, int BN>
 __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {

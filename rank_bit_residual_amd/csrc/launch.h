@@ -70,6 +70,8 @@ hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, vo
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
 // Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
+// Per-tensor INT, bits <= 4: 64x64 tiles, K split over the waves of a block (kstages = Kp/256).
+hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream);
 // MXFP4, bf16, B <= 64: K split over waves, weights streamed straight into registers.
 hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream);
 
