@@ -229,8 +229,9 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
  * svdq_profile_end, each svdq_linear call records a HIP event pair around every kernel it
  * launches whose stage bit is set in stage_mask, on the call's stream, for up to max_calls
  * calls. Stages: 0 = per-tensor max pre-pass (INT), 1 = smooth+quantise+down-projection,
- * 2 = split-K down reduction, 3 = residual GEMM + epilogue; a stage that did not run or was
- * not selected reads 0. Each event pair costs host time per call, so a throughput
+ * 2 = reserved (no kernel; split-K partials of the down-projection are summed in the GEMM
+ * epilogue), 3 = residual GEMM + epilogue; a stage that did not run or was not selected
+ * reads 0. Each event pair costs host time per call, so a throughput
  * measurement should select only the stages it needs.
  *   svdq_profile_begin: creates the events (host call; no device memory). EINVAL if
  *     max_calls < 1, stage_mask selects no stage or a bit above 3, or a session is already

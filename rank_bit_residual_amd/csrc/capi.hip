@@ -1,5 +1,5 @@
 // Device-side C ABI of libsvdq: argument validation, launch plans, workspace layout and the
-// launch sequences of svdq_linear (steps a+b, optional split-K reduction, c),
+// launch sequences of svdq_linear (steps a+b, then c, whose epilogue sums split-K partials),
 // svdq_quantize_activations, svdq_fake_quantize and svdq_smooth_inputs.
 #include <hip/hip_runtime.h>
 
@@ -26,7 +26,7 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
   p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
   p.amax_cols = (int)ceil_div(d.M, 2048);
-  p.amax_rows = (int)std::max<int64_t>(1, std::min<int64_t>(B, ceil_div(512, p.amax_cols)));
+  p.amax_rows = (int)std::min<int64_t>(65535, std::max<int64_t>(1, ceil_div(B, 8)));  // 8 rows per block
   p.amax_blocks = p.amax_cols * p.amax_rows;
   return p;
 }
@@ -286,13 +286,6 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, s), "activation quantise launch")))
     return st;
   tm.end(1);
-  if (d.rp > 0 && pl.k_chunks > 1) {
-    tm.begin(2);
-    if ((st = hip_status(launch_down_reduce(p.down_part, pl.k_chunks, (int)B, (int)d.rp, p.down, dtype, s),
-                         "down-projection reduce launch")))
-      return st;
-    tm.end(2);
-  }
   // (c): residual GEMM + epilogue
   GemmParams g{};
   g.acodes = ws + woff[WS_CODES];
@@ -306,6 +299,8 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.sx = sx;
   g.sr = (const float*)(bl + boff[SVDQ_SEC_RSCALES]);
   g.down = ws + woff[WS_DOWN];
+  g.down_part = (const float*)(ws + woff[WS_PARTIAL]);  // split-K partials, summed by the GEMM epilogue
+  g.down_chunks = pl.k_chunks;
   g.l2t = bl + boff[SVDQ_SEC_L2T];
   g.rp = (int)d.rp;
   g.y = y;

@@ -74,12 +74,13 @@ __device__ inline u32 pack_bf16x2(float a, float b) {
 }
 
 // True when t = RN(x * RN(1/s)) may round to a different bfloat16 than RN_f32(x / s):
-// t within 8 ulps of a bf16 rounding midpoint (low 16 bits in [0x7FF8, 0x8007]), or t not a
+// t within 3 ulps of a bf16 rounding midpoint (low 16 bits in [0x7FFD, 0x8003]), or t not a
 // normal number (zero, subnormal, infinite, NaN) while x is nonzero. The two differ by at
-// most 3 ulps when x * RN(1/s) is a normal product of normal factors.
+// most 2 ulps when x * RN(1/s) is a normal product of normal factors (each rounding adds at
+// most half an ulp of relative error 2^-24, and RN_f32(x / s) half an ulp).
 __device__ inline bool bf16_fast_risky(float t, float x) {
   const u32 u = __float_as_uint(t);
-  const bool near_mid = ((u + 8u) & 0xFFF0u) == 0x8000u;
+  const bool near_mid = (uint16_t)((uint16_t)u + (uint16_t)0x8003u) < (uint16_t)7u;
   // class mask: every class except -normal (bit 3) and +normal (bit 8)
   const bool not_normal = __builtin_amdgcn_classf(t, 0x2F7) && x != 0.f;
   return near_mid || not_normal;
@@ -158,6 +159,38 @@ __device__ inline void unpack_nibbles(u32 w, u32& lo, u32& hi) {
   // per byte t in [0,15]: ((t ^ 8) | 0x80) - 8 never borrows; ^ 0x80 yields int8(t - 16*(t>=8))
   lo = (((e ^ 0x08080808u) | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
   hi = (((o ^ 0x08080808u) | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+}
+
+// ---- the down-projection operand of the GEMM epilogues -----------------------------------
+// Eight consecutive entries down[row][k .. k+8) as bf16 (the operand of the up-projection
+// MFMAs): read directly, or, when the activation kernel split K over `chunks` blocks, the sum
+// of the f32 partials in chunk order 0, 1, ..., rounded once to bf16 (the same value the
+// unsplit kernel would store).
+__device__ inline v8bf down8_bf16(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
+  if (chunks <= 1)
+    return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(down) +
+                                                                   (int64_t)row * rp + k));
+  float s[8];
+  const float* src = part + (int64_t)row * rp + k;
+  const int64_t stride = (int64_t)B * rp;
+  {
+    const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w; s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  }
+  for (int c = 1; c < chunks; c++) {
+    const float4 a = *reinterpret_cast<const float4*>(src + c * stride), b = *reinterpret_cast<const float4*>(src + c * stride + 4);
+    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w; s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+  }
+  return __builtin_bit_cast(v8bf, v4i{(int)pack_bf16x2(s[0], s[1]), (int)pack_bf16x2(s[2], s[3]),
+                                      (int)pack_bf16x2(s[4], s[5]), (int)pack_bf16x2(s[6], s[7])});
+}
+// One entry down[row][k] as f32 (f32 io): direct, or the ordered sum of the partials.
+__device__ inline float down1_f32(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
+  if (chunks <= 1) return reinterpret_cast<const float*>(down)[(int64_t)row * rp + k];
+  const float* src = part + (int64_t)row * rp + k;
+  float s = src[0];
+  for (int c = 1; c < chunks; c++) s += src[(int64_t)c * B * rp];
+  return s;
 }
 
 // ---- wave / block reductions ------------------------------------------------------------

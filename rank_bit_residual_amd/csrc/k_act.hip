@@ -4,12 +4,13 @@
 //   * k_fake_quant  — per-tensor INT fake quantisation (dequantised values);
 //   * k_act_quant   — step (a)+(b) of the operator: X^ = D(x / scale), its INT or MXFP4
 //                     codes, and the low-rank down-projection X^ L1 on the matrix cores;
-//   * k_down_reduce — sums split-K partials of the down-projection in a fixed order.
 //
 // Pages: "SVDQuant Smoothing, Low-rank and Residual Quantization" ("Formula and
 // conventions" items 1 and 3: smoothing divides x by scale; the low-rank branch takes the
 // unquantised smoothed activations; per-tensor INT with ties to even) and the msModelSlim
 // SVDQuant guide, step 2 (MXFP4 per-block minmax activations).
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/svdq.h"
@@ -116,7 +117,25 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
   const int r0 = blockIdx.y * rpb, r1 = r0 + rpb < B ? r0 + rpb : B;
   float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (c0 < M) {
-    for (int r = r0; r < r1; r++) {
+    int r = r0;
+    if (DT::is_bf16 && vec_ok && c0 + 8 <= M) {
+      // eight rows per round, all loads issued before the maxima
+      for (; r + 8 <= r1; r += 8) {
+        uint4 w[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) w[u] = *reinterpret_cast<const uint4*>(x + (int64_t)(r + u) * ldx + c0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const u32 ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+          for (int h = 0; h < 4; h++) {
+            cm[2 * h] = fmaxf(cm[2 * h], fabsf(__uint_as_float(ws[h] << 16)));
+            cm[2 * h + 1] = fmaxf(cm[2 * h + 1], fabsf(__uint_as_float(ws[h] & 0xFFFF0000u)));
+          }
+        }
+      }
+    }
+    for (; r < r1; r++) {
       const typename DT::T* xr = x + (int64_t)r * ldx + c0;
       if (vec_ok && c0 + 8 <= M) {
         if constexpr (DT::is_bf16) {
@@ -216,29 +235,123 @@ struct ActLane {
   float sx, ysx, qmax;
 };
 
-// One 128-wide K step of one wave (see the kernel comment).
+// Broadcast of lane Q of each 16-lane row to the whole row (DPP row_newbcast; the compiler
+// folds it into the consuming VALU instruction).
+template <int Q>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + Q, 0xF, 0xF, false));
+}
+
+// Inputs of a full bf16 step that the caller loads one step ahead: the lane's 32 x values
+// (16 words of bf16 pairs), two reciprocals and two scales. Lane l = 16 g + q holds RN(1/s)
+// and s of columns k0 + 2 l and k0 + 2 l + 1, i.e. the pair q of the block that the lanes of
+// row g work on.
+struct FullIn {
+  u32 raw[16];
+  float2 y2, s2;
+};
+
+template <class T>
+__device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xrow, int lane, int g, int k0,
+                                          FullIn& in) {
+  const uint4* src = reinterpret_cast<const uint4*>(xrow + k0 + 32 * g);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint4 w = src[q];
+    in.raw[4 * q] = w.x; in.raw[4 * q + 1] = w.y; in.raw[4 * q + 2] = w.z; in.raw[4 * q + 3] = w.w;
+  }
+  in.y2 = *reinterpret_cast<const float2*>(p.recip + k0 + 2 * lane);
+  in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * lane);
+}
+
+// Pair Q (elements 2Q, 2Q+1 of the lane's block) of a full bf16 step: X^ = RN_bf16(RN_f32(x/s)).
+// The product t = RN(x * RN(1/s)) lies within 2 f32 ulps of RN_f32(x / s), so RN_bf16(t) is
+// exact unless bf16_fast_risky flags it; flagged elements take the correctly rounded division,
+// with the scale read on that rare path only.
+// Full bf16 steps: X^ = RN_bf16(RN_f32(x / s)) from t = RN(x * RN(1/s)). With RN(1/s) normal,
+// t lies within 2 f32 ulps of RN_f32(x / s) (within 1.5 subnormal spacings near zero, where
+// the bf16 spacing is far coarser; past the bf16 range both round to infinity), so RN_bf16(t)
+// is exact unless t lies within 3 ulps of a bf16 rounding midpoint: low 16 bits in
+// [0x7FFD, 0x8003], i.e. (low16 + 0x8003) mod 2^16 < 7. The fast pass tracks the minimum of
+// that quantity over the lane's 32 products with packed 16-bit ops and needs no branch; a lane
+// whose minimum is below 7 redoes its block with the correctly rounded division where needed,
+// from the scales loaded with the reciprocals (so the rare path waits on no memory).
+// amax16 keeps max |X^| as bf16 bit patterns in two 16-bit lanes (for non-negative values the
+// integer order is the numeric order).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <int Q>
+__device__ __forceinline__ void fast_pair(const FullIn& in, u32* xb, u16x2& mn, u16x2& amax16) {
+  const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
+  const float t0 = x0 * row_bcast<Q>(in.y2.x), t1 = x1 * row_bcast<Q>(in.y2.y);
+  const u32 lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);  // low halves
+  mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, lo) + (u16x2){0x8003, 0x8003});
+  const u32 pk = pack_bf16x2(t0, t1);
+  xb[Q] = pk;
+  amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
+}
+template <int... Q>
+__device__ __forceinline__ void fast_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& mn,
+                                           u16x2& amax16) {
+  (fast_pair<Q>(in, xb, mn, amax16), ...);
+}
+
+__device__ __forceinline__ bool near_bf16_midpoint(float t) {
+  return (uint16_t)((uint16_t)__float_as_uint(t) + (uint16_t)0x8003u) < (uint16_t)7u;
+}
+// Exact pass over pair Q for every lane of the wave (entered through a wave-uniform branch, so
+// the DPP broadcasts read active lanes; update_dpp is convergent and is not moved into the
+// divergent division below). Lanes without a flagged product reproduce their fast values.
+template <int Q>
+__device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& amax16) {
+  const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
+  const float y0 = row_bcast<Q>(in.y2.x), y1 = row_bcast<Q>(in.y2.y);
+  const float s0 = row_bcast<Q>(in.s2.x), s1 = row_bcast<Q>(in.s2.y);
+  float t0 = x0 * y0, t1 = x1 * y1;
+  if (near_bf16_midpoint(t0)) {
+    asm volatile("");  // rarely taken: keep it a branch
+    t0 = div_rn(x0, s0, y0);
+  }
+  if (near_bf16_midpoint(t1)) {
+    asm volatile("");
+    t1 = div_rn(x1, s1, y1);
+  }
+  const u32 pk = pack_bf16x2(t0, t1);
+  xb[Q] = pk;
+  amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
+}
+template <int... Q>
+__device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16) {
+  (exact_pair<Q>(in, xb, amax16), ...);
+}
+
+// One 128-wide K step of one wave (see the kernel comment). FULL bf16 steps take their x and
+// reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
 template <class DT, int FMT, bool NIB, bool FULL>
 __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                         int k0, v4f* acc) {
+                                         int k0, v4f* acc, const FullIn& in) {
   typedef typename DT::T T;
   constexpr int RW = DT::is_bf16 ? 16 : 32;
+  constexpr bool FAST = DT::is_bf16 && FULL;
   const int k = k0 + 32 * L.g;
   const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
 
   u32 raw[RW];
-  if (FULL) {
-    const uint4* src = reinterpret_cast<const uint4*>(xrow + k);
-#pragma unroll
-    for (int q = 0; q < RW / 4; q++) {
-      const uint4 w = src[q];
-      raw[4 * q] = w.x; raw[4 * q + 1] = w.y; raw[4 * q + 2] = w.z; raw[4 * q + 3] = w.w;
-    }
-  } else {
-    load_row32<DT>(xrow, k, p.M, p.x_vec_ok, raw);
-  }
   float s32[32], y32[32];
-  load_chan<FULL>(p.scale, k, p.M, 1.f, s32);
-  load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
+  if constexpr (!FAST) {
+    if (FULL) {
+      const uint4* src = reinterpret_cast<const uint4*>(xrow + k);
+#pragma unroll
+      for (int q = 0; q < RW / 4; q++) {
+        const uint4 w = src[q];
+        raw[4 * q] = w.x; raw[4 * q + 1] = w.y; raw[4 * q + 2] = w.z; raw[4 * q + 3] = w.w;
+      }
+    } else {
+      load_row32<DT>(xrow, k, p.M, p.x_vec_ok, raw);
+    }
+    load_chan<FULL>(p.scale, k, p.M, 1.f, s32);
+    load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
+  }
   // B operands of the down-projection for this step
   constexpr int NB = ACT_RCHUNK / 16;
   // (bf16: loaded with the step's other loads; f32 loads them at the MFMAs to save registers)
@@ -257,12 +370,32 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   // final rounding to the dtype (rounding is monotone, so it rounds to max |X^|).
   u32 xb[RW];
   float amax = 0.f;
-  if constexpr (DT::is_bf16) {
-    // bf16: X^ = RN_bf16(RN_f32(x / s)). The product t = RN(x * RN(1/s)) lies within 3 f32
-    // ulps of RN_f32(x / s), so RN_bf16(t) is already exact unless t sits within 8 ulps of a
-    // bf16 rounding midpoint (low 16 bits near 0x8000), or t is not a normal number while x is
-    // nonzero (underflow, or a scale whose reciprocal was not stored); those rare elements
-    // take the correctly rounded division.
+  if constexpr (FAST) {
+    u16x2 amax16 = {0, 0};
+    if (__all(in.y2.x != 0.f && in.y2.y != 0.f)) {
+      u16x2 mn = {0xFFFF, 0xFFFF};
+      fast_pairs(std::make_integer_sequence<int, 16>{}, in, xb, mn, amax16);
+      const bool lane_risky = (mn.x < mn.y ? mn.x : mn.y) < 7;
+      if (__any(lane_risky)) {
+        // rare: some product of the wave sits near a bf16 rounding midpoint (no memory access here)
+        amax16 = (u16x2){0, 0};
+        exact_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16);
+      }
+    } else {
+      // a stored reciprocal of 0 (scale outside [2^-90, 2^90]) among these columns: per-element rule
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) {
+        const float x0 = __uint_as_float(in.raw[j / 2] << 16), x1 = __uint_as_float(in.raw[j / 2] & 0xFFFF0000u);
+        const float t0 = smooth_bf16(x0, p.scale[k + j], p.recip[k + j]);
+        const float t1 = smooth_bf16(x1, p.scale[k + j + 1], p.recip[k + j + 1]);
+        const u32 pk = pack_bf16x2(t0, t1);
+        xb[j / 2] = pk;
+        amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
+      }
+    }
+    amax = __uint_as_float((u32)(amax16.x > amax16.y ? amax16.x : amax16.y) << 16);
+  } else if constexpr (DT::is_bf16) {
+    // tail step: same rule, per-lane reciprocals
 #pragma unroll
     for (int j = 0; j < 32; j += 2) {
       const float x0 = __uint_as_float(raw[j / 2] << 16), x1 = __uint_as_float(raw[j / 2] & 0xFFFF0000u);
@@ -364,13 +497,17 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   }
   if (L.nbl > 0) {
     if constexpr (DT::is_bf16) {
+      v8bf av[4];
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        const v8bf av = __builtin_bit_cast(v8bf, v4i{(int)xb[4 * s], (int)xb[4 * s + 1], (int)xb[4 * s + 2], (int)xb[4 * s + 3]});
+      for (int s = 0; s < 4; s++)
+        av[s] = __builtin_bit_cast(v8bf, v4i{(int)xb[4 * s], (int)xb[4 * s + 1], (int)xb[4 * s + 2], (int)xb[4 * s + 3]});
 #pragma unroll
-        for (int n = 0; n < NB; n++)
-          if (n < L.nbl) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, bw[n][s]), acc[n], 0, 0, 0);
-      }
+      for (int n = 0; n < NB; n++)
+        if (n < L.nbl) {
+#pragma unroll
+          for (int s = 0; s < 4; s++)
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], __builtin_bit_cast(v8bf, bw[n][s]), acc[n], 0, 0, 0);
+        }
     } else {
       // f32: 16x16x4 MFMAs; K-slice c of the tile holds k0 + 32 g + 4 c + e for e < 4
 #pragma unroll
@@ -434,11 +571,29 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
 #pragma unroll
   for (int n = 0; n < ACT_RCHUNK / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // full steps first (k0 ascending), then the tail and padding
+  // full steps first (k0 ascending), then the tail and padding; bf16 full steps load the next
+  // step's x and reciprocals before computing the current one
   const int kfull = p.x_vec_ok ? p.M : 0;
   int k0 = kbeg + 128 * wave;
-  for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc);
-  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false>(p, xrow, L, k0, acc);
+  FullIn cur;
+  if constexpr (DT::is_bf16) {
+    if (k0 < kend && k0 + 128 <= kfull) {
+      load_full(p, xrow, L.lane, L.g, k0, cur);
+      for (;;) {
+        const int kn = k0 + 128 * NW;
+        const bool more = kn < kend && kn + 128 <= kfull;
+        FullIn nxt;
+        if (more) load_full(p, xrow, L.lane, L.g, kn, nxt);
+        act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc, cur);
+        k0 = kn;
+        if (!more) break;
+        cur = nxt;
+      }
+    }
+  } else {
+    for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc, cur);
+  }
+  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false>(p, xrow, L, k0, acc, cur);
 
   if (L.nbl > 0) {
     // fixed-order sum of the waves' partial down-projections
@@ -474,26 +629,6 @@ __global__ void k_reciprocals(const float* __restrict__ scale, int M, float* __r
   }
 }
 
-// Fixed-order sum of the split-K partials; the independent loads of a thread are issued
-// together so their latencies overlap.
-template <class DT>
-__global__ void k_down_reduce(const float* __restrict__ part, int k_chunks, int B, int rp,
-                              typename DT::T* __restrict__ down) {
-  const int n = B * rp;
-  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += gridDim.x * blockDim.x) {
-    float s = 0.f;
-    int c = 0;
-    for (; c + 8 <= k_chunks; c += 8) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; q++) v[q] = part[(int64_t)(c + q) * n + idx];
-#pragma unroll
-      for (int q = 0; q < 8; q++) s += v[q];
-    }
-    for (; c < k_chunks; c++) s += part[(int64_t)c * n + idx];
-    down[idx] = DT::from_f32(s);
-  }
-}
 
 }  // namespace dev
 
@@ -596,14 +731,5 @@ hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_bloc
   return hipGetLastError();
 }
 
-hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, void* down, int dtype,
-                              hipStream_t stream) {
-  const int grid = grid_for((int64_t)B * rp, 1024);
-  if (dtype == SVDQ_F32)
-    k_down_reduce<F32><<<grid, 256, 0, stream>>>(part, k_chunks, B, rp, (float*)down);
-  else
-    k_down_reduce<BF16><<<grid, 256, 0, stream>>>(part, k_chunks, B, rp, (uint16_t*)down);
-  return hipGetLastError();
-}
 
 }  // namespace svdq

@@ -197,7 +197,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         for (int v = 0; v < 16; v++) f[mt][nt][v] = (float)acc[mt][nt][v] * scl;
   }
   if (p.rp > 0) {
-    const T* down = reinterpret_cast<const T*>(p.down);
     const T* l2t = reinterpret_cast<const T*>(p.l2t);
     int drow[2];
 #pragma unroll
@@ -210,7 +209,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         v8bf av[2], bv[2];
 #pragma unroll
         for (int q = 0; q < 2; q++) {
-          av[q] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)drow[q] * p.rp + kk + 8 * g));
+          av[q] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[q], kk + 8 * g);
           bv[q] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)(n0 + bcol[q]) * p.rp + kk + 8 * g));
         }
 #pragma unroll
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         float av[2], bv[2];
 #pragma unroll
         for (int q = 0; q < 2; q++) {
-          av[q] = down[(int64_t)drow[q] * p.rp + kk + g];
+          av[q] = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[q], kk + g);
           bv[q] = l2t[(int64_t)(n0 + bcol[q]) * p.rp + kk + g];
         }
 #pragma unroll

@@ -10,8 +10,9 @@
 // 16-row tiles. A 256-thread block owns 32 output columns (two 16-column tiles); its four waves
 // split K into quarters. Each lane loads its 32-code K block of a weight column straight into
 // registers in the MFMA B layout (every weight byte is used once, so there is no LDS staging),
-// eight K steps per batch so that many requests are in flight. The waves' partial tiles are
-// summed in LDS in a fixed order, then one wave adds down L2 with bf16 MFMAs, rounds and stores.
+// eight K steps per batch so that many requests are in flight. Each wave adds its share of
+// the up-projection down L2 (bf16 MFMAs) to its partial tile; the four partial tiles are summed
+// in LDS in a fixed order, and one wave rounds and stores.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/svdq.h"
@@ -105,7 +106,30 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
     step(wv, wsc, av, asc);
   }
 
-  // fixed-order sum of the four K quarters
+  // this wave's share of the up-projection, acc += down[rows, kk..kk+32) . L2^T[cols, kk..kk+32)^T
+  // for kk = 32 w, 32 w + 128, ... (16x16x32 bf16 MFMAs), before the partial tiles are summed
+  if (p.rp > 0) {
+    const T* l2t = reinterpret_cast<const T*>(p.l2t);
+    for (int kk = 32 * wave; kk < p.rp; kk += 128) {
+      v8bf bv[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++) {
+        int col = n0 + 16 * tt + i;
+        col = col < p.npad ? col : p.npad - 1;
+        bv[tt] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)col * p.rp + kk + 8 * g));
+      }
+#pragma unroll
+      for (int m = 0; m < MT; m++) {
+        int row = 16 * m + i;
+        row = row < p.B ? row : p.B - 1;
+        const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, row, kk + 8 * g);
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[tt], acc[m][tt], 0, 0, 0);
+      }
+    }
+  }
+
+  // fixed-order sum of the four waves' partial tiles
 #pragma unroll
   for (int m = 0; m < MT; m++)
 #pragma unroll
@@ -123,28 +147,6 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
         acc[m][tt][v] = ((red[0][m][tt][lane][v] + red[1][m][tt][lane][v]) + red[2][m][tt][lane][v]) +
                         red[3][m][tt][lane][v];
 
-  // up-projection: acc += down[rows, :] . L2^T[cols, :]^T on 16x16x32 bf16 MFMAs
-  if (p.rp > 0) {
-    const T* down = reinterpret_cast<const T*>(p.down);
-    const T* l2t = reinterpret_cast<const T*>(p.l2t);
-    for (int kk = 0; kk < p.rp; kk += 32) {
-      v8bf bv[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++) {
-        int col = n0 + 16 * tt + i;
-        col = col < p.npad ? col : p.npad - 1;
-        bv[tt] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)col * p.rp + kk + 8 * g));
-      }
-#pragma unroll
-      for (int m = 0; m < MT; m++) {
-        int row = 16 * m + i;
-        row = row < p.B ? row : p.B - 1;
-        const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)row * p.rp + kk + 8 * g));
-#pragma unroll
-        for (int tt = 0; tt < 2; tt++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[tt], acc[m][tt], 0, 0, 0);
-      }
-    }
-  }
   T* y = reinterpret_cast<T*>(p.y);
 #pragma unroll
   for (int m = 0; m < MT; m++)

@@ -166,20 +166,19 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   // ---- up-projection, rounding, masked store of quadrant (qi, qj)
   const int row0 = m0 + 32 * qi, col = n0 + 32 * qj + l32;
   if (p.rp > 0) {
-    const T* down = reinterpret_cast<const T*>(p.down);
     const T* l2t = reinterpret_cast<const T*>(p.l2t);
     int drow = row0 + l32;
     drow = drow < p.B ? drow : p.B - 1;
     const int bcol = col < p.npad ? col : p.npad - 1;
     if constexpr (DT::is_bf16) {
       for (int kk = 0; kk < p.rp; kk += 16) {
-        const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)drow * p.rp + kk + 8 * g));
+        const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow, kk + 8 * g);
         const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + kk + 8 * g));
         f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, f, 0, 0, 0);
       }
     } else {
       for (int kk = 0; kk < p.rp; kk += 2) {
-        const float av = down[(int64_t)drow * p.rp + kk + g];
+        const float av = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow, kk + g);
         const float bv = l2t[(int64_t)bcol * p.rp + kk + g];
         f = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, f, 0, 0, 0);
       }

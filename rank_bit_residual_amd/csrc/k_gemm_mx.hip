@@ -205,7 +205,6 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
 
   // ---- epilogue: up-projection on the matrix cores, one rounding, masked store
   if (p.rp > 0) {
-    const T* down = reinterpret_cast<const T*>(p.down);
     const T* l2t = reinterpret_cast<const T*>(p.l2t);
     int drow[C::MT], bcol[C::NT];
 #pragma unroll
@@ -222,7 +221,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
       v8bf av[C::MT], bv[C::NT];
 #pragma unroll
       for (int i = 0; i < C::MT; i++)
-        av[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(down + (int64_t)drow[i] * p.rp + kk + 8 * g));
+        av[i] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 8 * g);
 #pragma unroll
       for (int j = 0; j < C::NT; j++)
         bv[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 8 * g));

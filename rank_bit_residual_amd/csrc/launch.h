@@ -41,7 +41,9 @@ struct GemmParams {
   int kq;                  // Kp / 128: 128-code stages per row
   const float* sx;
   const float* sr;
-  const void* down;
+  const void* down;         // [B][rp] dtype, when down_chunks == 1
+  const float* down_part;   // [down_chunks][B][rp] f32 split-K partials of X^ L1, when down_chunks > 1
+  int down_chunks;
   const void* l2t;
   int rp;
   void* y;
@@ -65,8 +67,7 @@ hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t 
 // recip[m] = RN(1 / scale[m]) for scale[m] in [2^-90, 2^90], else 0 (the prepared RECIP section).
 hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream_t stream);
 hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream);
-hipError_t launch_down_reduce(const float* part, int k_chunks, int B, int rp, void* down, int dtype,
-                              hipStream_t stream);
+
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
 // Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
