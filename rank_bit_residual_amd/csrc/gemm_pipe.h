@@ -16,9 +16,24 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until the stage about to be read has landed: remaining_after = number of later
-// stages already issued (0 .. NS-2), LPS = loads per stage per wave. Loads complete in
-// issue order, so allowing LPS * remaining_after outstanding leaves the wanted stage done.
+// Wait until the stage about to be read has landed when up to D later stages may be in flight:
+// remaining_after = number of later stages already issued (0 .. D), LPS = loads per stage per
+// wave. Loads complete in issue order, so allowing LPS * remaining_after outstanding loads
+// leaves the wanted stage done.
+template <int LPS, int D>
+__device__ inline void wait_stage_upto(int remaining_after) {
+  if constexpr (D > 0) {
+    if (remaining_after >= D) {
+      wait_vmcnt<LPS * D>();
+      return;
+    }
+    wait_stage_upto<LPS, D - 1>(remaining_after);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// The same for a ring of NS buffers read with prefetch distance NS - 2.
 template <int LPS, int NS>
 __device__ inline void wait_stage(int remaining_after) {
   if constexpr (NS >= 5) {

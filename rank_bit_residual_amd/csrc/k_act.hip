@@ -115,6 +115,24 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
   __shared__ float sh[4];
   const int c0 = blockIdx.x * 2048 + threadIdx.x * 8;
   const int r0 = blockIdx.y * rpb, r1 = r0 + rpb < B ? r0 + rpb : B;
+  // this thread's scales and reciprocals, loaded together with x (one memory round trip)
+  float sc8[8], rc8[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    sc8[q] = 1.f;
+    rc8[q] = 0.f;
+  }
+  if (c0 + 8 <= M) {
+    const float4 s0 = *reinterpret_cast<const float4*>(scale + c0), s1 = *reinterpret_cast<const float4*>(scale + c0 + 4);
+    const float4 y0 = *reinterpret_cast<const float4*>(recip + c0), y1 = *reinterpret_cast<const float4*>(recip + c0 + 4);
+    sc8[0] = s0.x; sc8[1] = s0.y; sc8[2] = s0.z; sc8[3] = s0.w; sc8[4] = s1.x; sc8[5] = s1.y; sc8[6] = s1.z; sc8[7] = s1.w;
+    rc8[0] = y0.x; rc8[1] = y0.y; rc8[2] = y0.z; rc8[3] = y0.w; rc8[4] = y1.x; rc8[5] = y1.y; rc8[6] = y1.z; rc8[7] = y1.w;
+  } else {
+    for (int q = 0; q < 8 && c0 + q < M; q++) {
+      sc8[q] = scale[c0 + q];
+      rc8[q] = recip[c0 + q];
+    }
+  }
   float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (c0 < M) {
     int r = r0;
@@ -160,10 +178,7 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
   float a = 0.f;
 #pragma unroll
   for (int q = 0; q < 8; q++)
-    if (c0 + q < M) {
-      const float y = recip ? recip[c0 + q] : 0.f;
-      a = fmaxf(a, DT::to_f32(DT::from_f32(div_rn(cm[q], scale[c0 + q], y))));
-    }
+    if (c0 + q < M) a = fmaxf(a, DT::to_f32(DT::from_f32(div_rn(cm[q], sc8[q], rc8[q]))));
   a = block_max256(a, sh);
   if (threadIdx.x == 0) part[blockIdx.y * gridDim.x + blockIdx.x] = a;
 }

@@ -19,7 +19,8 @@
 // four waves split K: wave w takes the 16-byte chunks 2w and 2w+1 (two 32-code MFMA steps)
 // for the whole 64 x 64 tile, which keeps the nibble unpacking below the MFMA time. After
 // the K loop the four int32 partial tiles are summed through LDS (exact), and each wave
-// finishes one 32 x 32 quadrant: dequantise, up-projection, one rounding, masked store.
+// finishes one 32 x 32 quadrant (dequantise, up-projection, one rounding); the rounded tile
+// is staged in LDS and written with 16-byte stores.
 // LDS rows are 128 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16-byte reads
 // of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
 #include "device_common.h"
@@ -139,7 +140,34 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
     asm volatile("" ::: "memory");
   }
 
-  // ---- exact sum of the four waves' partial tiles: wave q then owns quadrant q = (i, j)
+  // ---- epilogue operands of this wave's quadrant q = (qi, qj), loaded before the exchange so
+  // their latency overlaps it (rank steps of 16 beyond RMAX are loaded when used)
+  const int qi = wave >> 1, qj = wave & 1;
+  const int row0 = m0 + 32 * qi, col = n0 + 32 * qj + l32;
+  int erow = row0 + l32;
+  erow = erow < p.B ? erow : p.B - 1;
+  const int bcol = col < p.npad ? col : p.npad - 1;
+  const T* l2t = reinterpret_cast<const T*>(p.l2t);
+  constexpr int RMAX = 4;
+  v8bf ua[RMAX], ub[RMAX];
+  float fa[2 * RMAX], fb[2 * RMAX];
+  if constexpr (DT::is_bf16) {
+#pragma unroll
+    for (int r = 0; r < RMAX; r++)
+      if (16 * r < p.rp) {
+        ua[r] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g);
+        ub[r] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + 16 * r + 8 * g));
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2 * RMAX; r++)
+      if (2 * r < p.rp) {
+        fa[r] = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 2 * r + g);
+        fb[r] = l2t[(int64_t)bcol * p.rp + 2 * r + g];
+      }
+  }
+
+  // ---- exact sum of the four waves' partial tiles; wave q then owns quadrant q
   __syncthreads();
   v4i* part = reinterpret_cast<v4i*>(smem);  // [wave][tile][v/4][lane] of 4 int32
 #pragma unroll
@@ -151,45 +179,61 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
         part[((wave * 4 + 2 * i + j) * 4 + v4) * 64 + lane] =
             v4i{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
   __syncthreads();
-  const int qi = wave >> 1, qj = wave & 1;
   v16f f;
   const float scl = p.sx[0] * p.sr[0];
 #pragma unroll
   for (int v4 = 0; v4 < 4; v4++) {
-    v4i s = part[((0 * 4 + wave) * 4 + v4) * 64 + lane];
+    v4i sum = part[((0 * 4 + wave) * 4 + v4) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; w++) s += part[((w * 4 + wave) * 4 + v4) * 64 + lane];
+    for (int w = 1; w < 4; w++) sum += part[((w * 4 + wave) * 4 + v4) * 64 + lane];
 #pragma unroll
-    for (int e = 0; e < 4; e++) f[4 * v4 + e] = ((float)s[e] * 0x1p-8f) * scl;
+    for (int e = 0; e < 4; e++) f[4 * v4 + e] = ((float)sum[e] * 0x1p-8f) * scl;
   }
 
-  // ---- up-projection, rounding, masked store of quadrant (qi, qj)
-  const int row0 = m0 + 32 * qi, col = n0 + 32 * qj + l32;
+  // ---- up-projection into the fp32 accumulators
   if (p.rp > 0) {
-    const T* l2t = reinterpret_cast<const T*>(p.l2t);
-    int drow = row0 + l32;
-    drow = drow < p.B ? drow : p.B - 1;
-    const int bcol = col < p.npad ? col : p.npad - 1;
     if constexpr (DT::is_bf16) {
-      for (int kk = 0; kk < p.rp; kk += 16) {
-        const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow, kk + 8 * g);
+#pragma unroll
+      for (int r = 0; r < RMAX; r++)
+        if (16 * r < p.rp) f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[r], ub[r], f, 0, 0, 0);
+      for (int kk = 16 * RMAX; kk < p.rp; kk += 16) {
+        const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, kk + 8 * g);
         const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + kk + 8 * g));
         f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, f, 0, 0, 0);
       }
     } else {
-      for (int kk = 0; kk < p.rp; kk += 2) {
-        const float av = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow, kk + g);
+#pragma unroll
+      for (int r = 0; r < 2 * RMAX; r++)
+        if (2 * r < p.rp) f = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[r], fb[r], f, 0, 0, 0);
+      for (int kk = 4 * RMAX; kk < p.rp; kk += 2) {
+        const float av = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, kk + g);
         const float bv = l2t[(int64_t)bcol * p.rp + kk + g];
         f = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, f, 0, 0, 0);
       }
     }
   }
-  if (col < p.N) {
-    T* y = reinterpret_cast<T*>(p.y);
+
+  // ---- round once, stage the 64 x 64 tile in LDS and write it with 16-byte stores
+  __syncthreads();  // every wave has read its partial sums
+  T* tile = reinterpret_cast<T*>(smem);
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int row = row0 + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (row < p.B) y[(int64_t)row * p.ldy + col] = DT::from_f32(f[v]);
+  for (int v = 0; v < 16; v++)
+    tile[(32 * qi + 8 * (v >> 2) + 4 * g + (v & 3)) * BN + 32 * qj + l32] = DT::from_f32(f[v]);
+  __syncthreads();
+  T* y = reinterpret_cast<T*>(p.y);
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = BN / EPC;        // chunks per tile row
+  const bool vec_ok = (p.ldy % EPC == 0) && (((uintptr_t)p.y & 15) == 0);
+  for (int c = t; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = c - r * CPR;
+    const int row = m0 + r, c0 = n0 + cc * EPC;
+    if (row >= p.B || c0 >= p.N) continue;
+    const T* src = tile + r * BN + cc * EPC;
+    T* dst = y + (int64_t)row * p.ldy + c0;
+    if (vec_ok && c0 + EPC <= p.N) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    } else {
+      for (int e = 0; e < EPC && c0 + e < p.N; e++) dst[e] = src[e];
     }
   }
 }
