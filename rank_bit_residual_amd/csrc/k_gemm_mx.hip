@@ -261,8 +261,10 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
     if (vec_ok && col + 8 <= p.N) {
       *reinterpret_cast<uint4*>(dst) = v;
     } else {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-      for (int q = 0; q < 8 && col + q < p.N; q++) dst[q] = e[q];
+      const u32 w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 8; q++)
+        if (col + q < p.N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
     }
   }
 }
@@ -290,6 +292,10 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
 // is not covered, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
   if (dtype != SVDQ_BF16 || p.B < 256) return hipErrorNotSupported;
+  // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
+  // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192).
+  const int tiles_m = (p.B + 255) / 256;
+  if (p.N % 256 == 0 && tiles_m * (p.N / 256) >= 512) return launch_mx_t<256, 256>(p, stream);
   if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, stream);
   return launch_mx_t<256, 256>(p, stream);
 }
