@@ -9,7 +9,8 @@
 // item 3; "flashinfer.gemm.svdquant_linear" (residual GEMM with the low-rank up-projection in
 // its epilogue: prior art for this split); msModelSlim SVDQuant guide step 2 (MXFP4 per block).
 //
-// Structure: a BM x BN output tile per 256-thread block (2 x 2 waves). K advances in stages of
+// Structure: a BM x BN output tile per 512-thread block (4 x 2 waves, two per SIMD so that one
+// wave's LDS and barrier waits overlap the other's MFMAs). K advances in stages of
 // 128 codes (64 bytes per row). Stages land in a ring of NS LDS buffers through direct
 // global->LDS loads (global_load_lds_dwordx4 / _dword), issued NS-1 stages ahead; each wave
 // waits on its own vmcnt for the stage it is about to read, then one s_barrier makes every
@@ -26,17 +27,19 @@ namespace dev {
 
 template <int BM, int BN>
 struct MxCfg {
+  static constexpr int NWV = 8, WN = 2, WM = NWV / WN;  // 4 x 2 waves, two per SIMD
   static constexpr int SB = 64;               // bytes per row per stage (128 FP4 codes)
-  static constexpr int TM = BM / 2, TN = BN / 2;  // per-wave tile
+  static constexpr int TM = BM / WM, TN = BN / WN;  // per-wave tile
   static constexpr int MT = TM / 32, NT = TN / 32;
   static constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // wave-wide 16-byte DMA loads
-  static_assert(A_INSTR % 4 == 0 && B_INSTR % 4 == 0, "tile rows must fill whole wave-wide loads");
-  static constexpr int A_PER_WAVE = A_INSTR / 4;
-  static constexpr int B_PER_WAVE = (B_INSTR + 3) / 4;
+  static_assert(A_INSTR % NWV == 0, "tile rows must fill whole wave-wide loads");
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole 32 x 32 MFMA tiles");
+  static constexpr int A_PER_WAVE = A_INSTR / NWV;
+  static constexpr int B_PER_WAVE = (B_INSTR + NWV - 1) / NWV;
   static constexpr int SCALE_BYTES = 1024;         // 256 rows x 4 bytes, per operand (padded)
-  static constexpr int STAGE = A_BYTES + B_PER_WAVE * 4 * 1024 + 2 * SCALE_BYTES;
-  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE + 2;  // per wave
+  static constexpr int STAGE = A_BYTES + B_PER_WAVE * NWV * 1024 + 2 * SCALE_BYTES;
+  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE + 1;  // per wave (one scale load)
   static constexpr int NS = 4;    // LDS ring depth
   static constexpr int DIST = 2;  // stages in flight ahead of the one being computed
   static constexpr int SMEM = NS * STAGE;
@@ -45,13 +48,13 @@ struct MxCfg {
 __device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 template <class DT, int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
+__global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   typedef MxCfg<BM, BN> C;
   typedef typename DT::T T;
   extern __shared__ __align__(1024) uint8_t smem[];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- tile order: XCD-aware (blocks i, i+8, ... share an XCD) and grouped by 4 row tiles
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
   int a_dst[C::A_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < C::A_PER_WAVE; j++) {
-    const int u = wave + 4 * j;  // instruction index: 16 rows x 64 bytes
+    const int u = wave + C::NWV * j;  // instruction index: 16 rows x 64 bytes
     const int q = u * 64 + lane;
     const int row = q >> 2, phys = q & 3;
     const int chunk = phys ^ ((row >> 2) & 3);
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
   int b_dst[C::B_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < C::B_PER_WAVE; j++) {
-    int u = wave + 4 * j;
+    int u = wave + C::NWV * j;
     const bool real = u < C::B_INSTR;
     const int q = (real ? u : 0) * 64 + lane;
     const int row = q >> 2, phys = q & 3;
@@ -95,15 +98,17 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
     b_src[j] = p.wcodes + (int64_t)gr * p.ldw + chunk * 16;
     b_dst[j] = C::A_BYTES + u * 1024;  // u >= B_INSTR lands in the padding after B
   }
-  // scales (stage-tiled): wave w loads the 64-row group w of the A tile and of the B tile,
-  // 256 contiguous bytes per stage; groups past the data clamp to the last one (discarded)
-  int ga = (m0 >> 6) + wave;
+  // scales (stage-tiled): waves 0-3 load the 64-row groups 0-3 of the A tile, waves 4-7 those of
+  // the B tile, 256 contiguous bytes per stage; groups past the data clamp to the last one
+  // (discarded)
+  const int sw = wave & 3;
+  int ga = (m0 >> 6) + sw;
   ga = ga < p.ascale_groups ? ga : p.ascale_groups - 1;
   const uint8_t* sa_src = p.ascales + ((int64_t)ga * p.kq << 8) + lane * 4;
-  int gb = (n0 >> 6) + (64 * wave < BN ? wave : 0);
+  int gb = (n0 >> 6) + (64 * sw < BN ? sw : 0);
   gb = gb < (p.npad >> 6) ? gb : (p.npad >> 6) - 1;
   const uint8_t* sb_src = p.wscales + ((int64_t)gb * p.kq << 8) + lane * 4;
-  const int s_off_a = C::A_BYTES + C::B_PER_WAVE * 4 * 1024;
+  const int s_off_a = C::A_BYTES + C::B_PER_WAVE * C::NWV * 1024;
   const int s_off_b = s_off_a + C::SCALE_BYTES;
 
   auto issue = [&](int st) {
@@ -114,8 +119,10 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < C::B_PER_WAVE; j++)
       __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + st * C::SB), (lds_ptr_t)(base + b_dst[j]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(sa_src + st * 256), (lds_ptr_t)(base + s_off_a + wave * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(sb_src + st * 256), (lds_ptr_t)(base + s_off_b + wave * 256), 4, 0, 0);
+    if (wave < 4)
+      __builtin_amdgcn_global_load_lds((const void*)(sa_src + st * 256), (lds_ptr_t)(base + s_off_a + sw * 256), 4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(sb_src + st * 256), (lds_ptr_t)(base + s_off_b + sw * 256), 4, 0, 0);
   };
 
   v16f acc[C::MT][C::NT];
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx(GemmParams p) {
   T* y = reinterpret_cast<T*>(p.y);
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   const bool vec_ok = (p.ldy % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
-  for (int c = t; c < BM * CPR; c += 256) {
+  for (int c = t; c < BM * CPR; c += 64 * C::NWV) {
     const int r = c / CPR, cc = c - r * CPR;
     const int row = m0 + r, col = n0 + cc * 8;
     if (row >= p.B || col >= p.N) continue;
@@ -284,7 +291,7 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_gemm_mx<BF16, BM, BN><<<tiles, 256, C::SMEM, stream>>>(p);
+  k_gemm_mx<BF16, BM, BN><<<tiles, 64 * C::NWV, C::SMEM, stream>>>(p);
   return hipGetLastError();
 }
 
