@@ -39,6 +39,8 @@ def gemm_kernel(wl, B):
         return "k_gemm_decode_mx", os.path.join(CSRC, "k_gemm_decode.hip")
     if wl.fmt == "mx" and wl.dtype == "bf16" and B >= 256:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
+    if wl.fmt == "int" and wl.bits <= 4:
+        return "k_gemm_int4", os.path.join(CSRC, "k_gemm_int.hip")
     return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 
 
@@ -97,7 +99,7 @@ def cpu_baseline(wl, x, s, prep, budget_s=10.0):
     if rows < wl.B and one < budget_s / 4:
         rows = min(wl.B, int(rows * max(1.0, (budget_s / 4) / max(one, 1e-3))))
     reps, done, t_total = 0, 0.0, 0.0
-    while t_total < budget_s and reps < 50:
+    while t_total < budget_s and reps < 10000:
         t0 = time.perf_counter()
         O.forward_ref(x[:rows], s, left, right, res, wl.fmt, wl.bits, wl.dtype)
         t_total += time.perf_counter() - t0
