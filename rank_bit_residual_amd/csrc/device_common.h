@@ -97,6 +97,20 @@ __device__ inline float smooth_bf16(float x, float s, float y) {
   return t;
 }
 
+// x / s by q0 = RN(x y) and two Newton-Markstein corrections, without range branches, for
+// y = RN(1/s) with s in [2^-90, 2^90]. Rounded on to bfloat16, the result equals
+// RN_bf16(RN_f32(x / s)) for every finite bf16 x (including zeros and subnormals), except that
+// a quotient that overflows comes out as NaN instead of +-infinity; callers replace those.
+// The sign of x is restored for zeros (the corrections would turn -0 into +0).
+__device__ inline float div_markstein(float x, float s, float y) {
+  float q = x * y;
+  float r = __builtin_fmaf(-s, q, x);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-s, q, x);
+  q = __builtin_fmaf(r, y, q);
+  return __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
+}
+
 // ---- MXFP4 ------------------------------------------------------------------------------
 // Shared exponent of a 32-element block from its max magnitude a: the smallest e with
 // a <= 6 * 2^e, clamped to [-127, 127] (E8M0 byte = e + 127). For normal a = 1.m * 2^E the

@@ -283,54 +283,19 @@ __device__ __forceinline__ void load_full(const ActParams& p, const T* __restric
 // The product t = RN(x * RN(1/s)) lies within 2 f32 ulps of RN_f32(x / s), so RN_bf16(t) is
 // exact unless bf16_fast_risky flags it; flagged elements take the correctly rounded division,
 // with the scale read on that rare path only.
-// Full bf16 steps: X^ = RN_bf16(RN_f32(x / s)) from t = RN(x * RN(1/s)). With RN(1/s) normal,
-// t lies within 2 f32 ulps of RN_f32(x / s) (within 1.5 subnormal spacings near zero, where
-// the bf16 spacing is far coarser; past the bf16 range both round to infinity), so RN_bf16(t)
-// is exact unless t lies within 3 ulps of a bf16 rounding midpoint: low 16 bits in
-// [0x7FFD, 0x8003], i.e. (low16 + 0x8003) mod 2^16 < 7. The fast pass tracks the minimum of
-// that quantity over the lane's 32 products with packed 16-bit ops and needs no branch; a lane
-// whose minimum is below 7 redoes its block with the correctly rounded division where needed,
-// from the scales loaded with the reciprocals (so the rare path waits on no memory).
+// Full bf16 steps: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein, with the
+// reciprocal and the scale of each column broadcast from the lane that loaded them (DPP,
+// while the whole wave is active). Branch-free; an overflowing quotient shows up as a bf16 NaN
+// and is replaced by +-infinity afterwards (a wave-uniform branch that real data never takes).
 // amax16 keeps max |X^| as bf16 bit patterns in two 16-bit lanes (for non-negative values the
 // integer order is the numeric order).
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int Q>
-__device__ __forceinline__ void fast_pair(const FullIn& in, u32* xb, u16x2& mn, u16x2& amax16) {
-  const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
-  const float t0 = x0 * row_bcast<Q>(in.y2.x), t1 = x1 * row_bcast<Q>(in.y2.y);
-  const u32 lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);  // low halves
-  mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, lo) + (u16x2){0x8003, 0x8003});
-  const u32 pk = pack_bf16x2(t0, t1);
-  xb[Q] = pk;
-  amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
-}
-template <int... Q>
-__device__ __forceinline__ void fast_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& mn,
-                                           u16x2& amax16) {
-  (fast_pair<Q>(in, xb, mn, amax16), ...);
-}
-
-__device__ __forceinline__ bool near_bf16_midpoint(float t) {
-  return (uint16_t)((uint16_t)__float_as_uint(t) + (uint16_t)0x8003u) < (uint16_t)7u;
-}
-// Exact pass over pair Q for every lane of the wave (entered through a wave-uniform branch, so
-// the DPP broadcasts read active lanes; update_dpp is convergent and is not moved into the
-// divergent division below). Lanes without a flagged product reproduce their fast values.
-template <int Q>
 __device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& amax16) {
   const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
-  const float y0 = row_bcast<Q>(in.y2.x), y1 = row_bcast<Q>(in.y2.y);
-  const float s0 = row_bcast<Q>(in.s2.x), s1 = row_bcast<Q>(in.s2.y);
-  float t0 = x0 * y0, t1 = x1 * y1;
-  if (near_bf16_midpoint(t0)) {
-    asm volatile("");  // rarely taken: keep it a branch
-    t0 = div_rn(x0, s0, y0);
-  }
-  if (near_bf16_midpoint(t1)) {
-    asm volatile("");
-    t1 = div_rn(x1, s1, y1);
-  }
+  const float t0 = div_markstein(x0, row_bcast<Q>(in.s2.x), row_bcast<Q>(in.y2.x));
+  const float t1 = div_markstein(x1, row_bcast<Q>(in.s2.y), row_bcast<Q>(in.y2.y));
   const u32 pk = pack_bf16x2(t0, t1);
   xb[Q] = pk;
   amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
@@ -338,6 +303,14 @@ __device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& ama
 template <int... Q>
 __device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16) {
   (exact_pair<Q>(in, xb, amax16), ...);
+}
+
+// Replace bf16 NaNs (quotients that overflowed) by infinity with the sign of x.
+__device__ __forceinline__ u32 nan_to_inf_pair(u32 pk, u32 raw) {
+  u32 r = pk;
+  if ((pk & 0x7FFFu) > 0x7F80u) r = (r & 0xFFFF0000u) | 0x7F80u | ((raw >> 0) & 0x8000u);
+  if ((pk & 0x7FFF0000u) > 0x7F800000u) r = (r & 0x0000FFFFu) | 0x7F800000u | (raw & 0x80000000u);
+  return r;
 }
 
 // One 128-wide K step of one wave (see the kernel comment). FULL bf16 steps take their x and
@@ -388,13 +361,15 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   if constexpr (FAST) {
     u16x2 amax16 = {0, 0};
     if (__all(in.y2.x != 0.f && in.y2.y != 0.f)) {
-      u16x2 mn = {0xFFFF, 0xFFFF};
-      fast_pairs(std::make_integer_sequence<int, 16>{}, in, xb, mn, amax16);
-      const bool lane_risky = (mn.x < mn.y ? mn.x : mn.y) < 7;
-      if (__any(lane_risky)) {
-        // rare: some product of the wave sits near a bf16 rounding midpoint (no memory access here)
+      exact_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16);
+      if (__any((amax16.x > amax16.y ? amax16.x : amax16.y) > 0x7F80)) {
+        // an overflowing quotient somewhere in the wave (never for real activations)
         amax16 = (u16x2){0, 0};
-        exact_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16);
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+          xb[q] = nan_to_inf_pair(xb[q], in.raw[q]);
+          amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, xb[q] & 0x7FFF7FFFu));
+        }
       }
     } else {
       // a stored reciprocal of 0 (scale outside [2^-90, 2^90]) among these columns: per-element rule

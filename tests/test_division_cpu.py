@@ -65,6 +65,20 @@ static int int_code_fast(float z, float sx, float ysx, float qmax) {
   return (int)fminf(fmaxf(rintf(d), -qmax), qmax);
 }
 static int int_code_ref(float z, float sx, float qmax) { return (int)fminf(fmaxf(rintf(z / sx), -qmax), qmax); }
+/* the activation kernel's branch-free rule: q0 = x y, two Markstein corrections, the sign of x
+   restored, then an overflow (NaN) replaced by infinity with the sign of x */
+static float markstein_bf16(float x, float s, float y) {
+  float q = x * y;
+  float r = fmaf(-s, q, x);
+  q = fmaf(r, y, q);
+  r = fmaf(-s, q, x);
+  q = fmaf(r, y, q);
+  uint32_t uq, ux; memcpy(&uq, &q, 4); memcpy(&ux, &x, 4);
+  uq |= ux & 0x80000000u;
+  memcpy(&q, &uq, 4);
+  if (isnan(q)) q = copysignf(INFINITY, x);
+  return bf16_round(q);
+}
 int main(int argc, char** argv) {
   if (argc > 2) {                          /* fast bf16 smoothing and INT codes */
     FILE* f = fopen(argv[1], "rb");
@@ -78,6 +92,10 @@ int main(int argc, char** argv) {
         for (int sg = 0; sg < 2; sg++, x = -x) {
           float a = smooth_bf16_fast(x, s, y), b = bf16_round(x / s);
           if (memcmp(&a, &b, 4)) { if (bad < 5) printf("bad smooth x=%a s=%a got %a want %a\n", x, s, a, b); bad++; }
+          if (y != 0.0f) {
+            float m = markstein_bf16(x, s, y);
+            if (memcmp(&m, &b, 4)) { if (bad < 5) printf("bad markstein x=%a s=%a got %a want %a\n", x, s, m, b); bad++; }
+          }
           if (y != 0.0f && fabsf(x) >= 0x1p-30f && fabsf(x) <= 0x1p30f) { slow += risky(x * y, y); typical++; }
           total++;
         }
