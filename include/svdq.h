@@ -127,9 +127,12 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
  * each 256-byte aligned), with Kp = M rounded up to 256, Np = N rounded up to 256 and
  * rp = rank rounded up to 32 (zero padding is exact: padded codes and factors are 0):
  *   SVDQ_SEC_SCALE   float32 [M]       the smoothing scale (divisor of x)
- *   SVDQ_SEC_RCODES  uint8 [Np, Kp/2]  R^T codes, K-contiguous per output column n:
- *                    two 4-bit codes per byte, even k in the low nibble (MX: E2M1;
- *                    INT bits<=4: two's-complement nibbles) — or int8 [Np, Kp] for INT bits>4
+ *   SVDQ_SEC_RCODES  R^T codes, two 4-bit codes per byte with even k in the low nibble
+ *                    (MX: E2M1; INT bits<=4: two's-complement nibbles), or int8 for INT
+ *                    bits>4. INT: [Np, Kp/2] (or [Np, Kp]) bytes, K-contiguous per output
+ *                    column n. MX: Np * Kp/2 bytes in 1 KB tiles, byte j (codes 2j, 2j+1)
+ *                    of column n at ((n/16) * (Kp/128) + j/64) * 1024 + (n%16) * 64 + j%64
+ *                    (each 16-column x 128-code block is contiguous: one wave-wide load)
  *   SVDQ_SEC_RSCALES MX: Np * Kp/32 E8M0 bytes (e + 127), one per 32-block of column n,
  *                    stage-tiled: the byte of (n, block kb) sits at
  *                    ((n/64) * (Kp/128) + kb/4) * 256 + (n%64) * 4 + kb%4

@@ -21,8 +21,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef uint32_t u32;
 typedef uint64_t u64;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // ---- storage dtypes ---------------------------------------------------------------------
 struct F32 {
@@ -155,6 +157,12 @@ __device__ inline u32 fp4_pack8_bf16(const u32* pairs, float scale) {
 // loads a stage's scales for 64 rows with four 64-byte requests.
 __host__ __device__ inline int64_t mx_scale_tiled_index(int64_t row, int64_t kb, int64_t kq) {
   return (((row >> 6) * kq + (kb >> 2)) << 8) + ((row & 63) << 2) + (kb & 3);
+}
+// Prepared MXFP4 residual codes come in 1 KB tiles (16 columns x 64 bytes = 128 codes):
+// byte j of column n at ((n/16) * kq + j/64) * 1024 + (n%16) * 64 + j%64. Offset of
+// column n's first K step; step s adds 1024 * s.
+__host__ __device__ inline int64_t mx_code_tile_offset(int64_t n, int64_t kq) {
+  return (((n >> 4) * kq) << 10) + ((n & 15) << 6);
 }
 
 // ---- per-tensor INT ---------------------------------------------------------------------

@@ -145,6 +145,13 @@ inline int64_t mx_tiled(int64_t row, int64_t kb, int64_t kq) {
   return (((row >> 6) * kq + (kb >> 2)) << 8) + ((row & 63) << 2) + (kb & 3);
 }
 
+// Tiled MXFP4 residual codes: byte j (codes 2j, 2j+1) of column n sits at
+// ((n/16) * kq + j/64) * 1024 + (n%16) * 64 + j%64, i.e. every 16-column x 128-code block
+// is 1 KB contiguous, the operand of one wave-wide load.
+inline int64_t mx_code_tiled(int64_t n, int64_t j, int64_t kq) {
+  return (((n >> 4) * kq + (j >> 6)) << 10) + ((n & 15) << 6) + (j & 63);
+}
+
 int validate_prepare(int64_t M, int64_t N, int64_t ldw, int64_t rank, int fmt, int bits, int dtype) {
   int st = check_dtype(dtype);
   if (st) return st;
@@ -302,7 +309,7 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
         const int e = mx_exponent(a);
         sc[mx_tiled(n, b, d.Kp / 128)] = (uint8_t)(e + 127);
         for (int64_t m = m0; m < m1; m++)
-          codes[n * crow + m / 2] |= (uint8_t)(e2m1_code(R[m * N + n], e) << (4 * (m & 1)));
+          codes[mx_code_tiled(n, m / 2, d.Kp / 128)] |= (uint8_t)(e2m1_code(R[m * N + n], e) << (4 * (m & 1)));
       }
     }
   }

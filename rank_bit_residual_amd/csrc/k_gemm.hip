@@ -52,7 +52,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     int ra = m0 + ld_row + 32 * j;
     ra = ra < p.B ? ra : p.B - 1;
     a_src[j] = p.acodes + (int64_t)ra * p.lda + ld_ch * 16;
-    b_src[j] = p.wcodes + (int64_t)(n0 + ld_row + 32 * j) * p.ldw + ld_ch * 16;
+    const int n = n0 + ld_row + 32 * j;
+    // MX weight codes are tiled (1 KB per 16 columns x 128 codes; a 256-code stage spans two
+    // tiles 1 KB apart); INT codes are K-contiguous rows
+    b_src[j] = MX ? p.wcodes + mx_code_tile_offset(n, p.kq) + (ld_ch & 3) * 16 + (ld_ch >> 2) * 1024
+                  : p.wcodes + (int64_t)n * p.ldw + ld_ch * 16;
   }
   // scale bytes of one row for a 256-code stage: 4-block groups 2st and 2st+1 (tiled layout)
   const uint8_t* s_src = nullptr;
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       ra_[j] = *reinterpret_cast<const uint4*>(a_src[j] + st * SB);
-      rb_[j] = *reinterpret_cast<const uint4*>(b_src[j] + st * SB);
+      rb_[j] = *reinterpret_cast<const uint4*>(b_src[j] + (int64_t)st * (MX ? 2048 : SB));
     }
     if (MX)
       rs_ = (u64) * reinterpret_cast<const u32*>(s_src + (int64_t)(2 * st) * 256) |

@@ -7,12 +7,16 @@
 // its epilogue); msModelSlim SVDQuant guide step 2 (MXFP4 per block).
 //
 // Structure: v_mfma_scale_f32_16x16x128_f8f6f4 with the (up to 64) batch rows as the M side in
-// 16-row tiles. A 256-thread block owns 32 output columns (two 16-column tiles); its four waves
-// split K into quarters. Each lane loads its 32-code K block of a weight column straight into
-// registers in the MFMA B layout (every weight byte is used once, so there is no LDS staging),
-// eight K steps per batch so that many requests are in flight. Each wave adds its share of
-// the up-projection down L2 (bf16 MFMAs) to its partial tile; the four partial tiles are summed
-// in LDS in a fixed order, and one wave rounds and stores.
+// 16-row tiles. A block owns 32 output columns (two 16-column tiles); its eight waves (two per
+// SIMD; four waves for batches above 32 rows) split K evenly. Each lane loads its 32-code K
+// block of a weight column straight into registers in the MFMA B layout (every weight byte is
+// used once, so there is no LDS staging); the prepared codes are tiled so that a 16-column
+// step is one contiguous 1 KB load. Eight K steps per batch so that many requests are in
+// flight; at 16 rows and K = 8192 each wave's whole share is one batch. Each wave adds its share of
+// the up-projection down L2 (16 rank columns per wave, bf16 MFMAs) to its partial tile; those
+// operands are requested ahead of the residual codes and multiplied while the codes are still
+// in flight. The partial tiles are summed in LDS in a fixed order, and one wave rounds and
+// stores.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/svdq.h"
@@ -21,17 +25,19 @@ namespace svdq {
 namespace dev {
 
 constexpr int DEC_COLS = 32;   // output columns per block
-constexpr int DEC_BATCH = 8;   // K steps per load batch
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
+// MT: 16-row tiles of the batch; DEC_WAVES: waves per block, each taking 1/DEC_WAVES of K
+// (eight, two per SIMD, while the registers allow; four with four row tiles)
+template <int MT, int DEC_WAVES>
+__global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p) {
   typedef BF16::T T;
-  __shared__ float red[4][MT][2][64][4];
+  constexpr int DEC_BATCH = MT >= 2 ? 4 : 8;  // K steps per load batch
+  __shared__ float red[DEC_WAVES][MT][2][64][4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * DEC_COLS;
   const int nst = p.kq;  // 128-code K steps
-  const int s0 = (wave * nst) >> 2, s1 = ((wave + 1) * nst) >> 2;
+  const int s0 = (wave * nst) / DEC_WAVES, s1 = ((wave + 1) * nst) / DEC_WAVES;
 
   // weight columns of the two tiles and activation rows of the MT tiles for this lane
   const uint8_t* wsrc[2];
@@ -40,7 +46,7 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
   for (int tt = 0; tt < 2; tt++) {
     int col = n0 + 16 * tt + i;
     col = col < p.npad ? col : p.npad - 1;
-    wsrc[tt] = p.wcodes + (int64_t)col * p.ldw + g * 16;
+    wsrc[tt] = p.wcodes + mx_code_tile_offset(col, p.kq) + g * 16;  // + 1024 per K step
     wssrc[tt] = p.wscales + mx_scale_tiled_index(col, 0, p.kq);
   }
   const uint8_t* asrc[MT];
@@ -70,32 +76,108 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
             (int)(asc[m] >> (8 * g)), 0, (int)(wsc[tt] >> (8 * g)));
   };
 
-  int s = s0;
-  for (; s + DEC_BATCH <= s1; s += DEC_BATCH) {
+  // ---- up-projection operands. Wave w owns rank columns [16 w + UPW j, +16) for j = 0, 1, ...
+  // (16x16x16 bf16 MFMAs: lane (i, g) holds down[row i][4 g .. 4 g + 3] and L2^T[col i][same]).
+  // down is either the finished [B][rp] matrix or the sum, in chunk order, of the f32 split-K
+  // partials, rounded once to bf16. Round j = 0 is loaded before the residual codes, so its
+  // requests travel together with them and its MFMAs run while the codes are still in flight.
+  constexpr int UPW = 16 * DEC_WAVES;
+  constexpr int PF = MT >= 4 ? 2 : 8 / MT;  // split-K partials prefetched per round (the rest are summed after)
+  const T* l2t = reinterpret_cast<const T*>(p.l2t);
+  int urow[MT], ucol[2];
+#pragma unroll
+  for (int m = 0; m < MT; m++) urow[m] = 16 * m + i < p.B ? 16 * m + i : p.B - 1;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++) {
+    const int col = n0 + 16 * tt + i;
+    ucol[tt] = col < p.npad ? col : p.npad - 1;
+  }
+  struct UpOps {
+    v4s b[2];
+    v4f part[MT][PF];  // split-K partials (down_chunks > 1)
+    v4s d[MT];         // finished down entries (down_chunks <= 1)
+  };
+  auto up_load = [&](UpOps& u, int kk) {
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) u.b[tt] = *reinterpret_cast<const v4s*>(l2t + (int64_t)ucol[tt] * p.rp + kk);
+    if (p.down_chunks <= 1) {
+#pragma unroll
+      for (int m = 0; m < MT; m++)
+        u.d[m] = *reinterpret_cast<const v4s*>(reinterpret_cast<const T*>(p.down) + (int64_t)urow[m] * p.rp + kk);
+    } else {
+      const int64_t stride = (int64_t)p.B * p.rp;
+#pragma unroll
+      for (int m = 0; m < MT; m++)
+#pragma unroll
+        for (int c = 0; c < PF; c++)
+          if (c < p.down_chunks)
+            u.part[m][c] = *reinterpret_cast<const v4f*>(p.down_part + c * stride + (int64_t)urow[m] * p.rp + kk);
+    }
+  };
+  auto up_mma = [&](const UpOps& u, int kk) {
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      v4s a;
+      if (p.down_chunks <= 1) {
+        a = u.d[m];
+      } else {
+        v4f sum = u.part[m][0];
+#pragma unroll
+        for (int c = 1; c < PF; c++)
+          if (c < p.down_chunks) sum += u.part[m][c];
+        const int64_t stride = (int64_t)p.B * p.rp;
+        for (int c = PF; c < p.down_chunks; c++)
+          sum += *reinterpret_cast<const v4f*>(p.down_part + c * stride + (int64_t)urow[m] * p.rp + kk);
+        const u32 lo = pack_bf16x2(sum[0], sum[1]), hi = pack_bf16x2(sum[2], sum[3]);
+        a = __builtin_bit_cast(v4s, v2u{lo, hi});
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, u.b[tt], acc[m][tt], 0, 0, 0);
+    }
+  };
+  const int kk0 = 16 * wave + 4 * g;  // this lane's first rank column of round 0
+  const bool up0 = 16 * wave < p.rp;
+  UpOps u0;
+  if (up0) up_load(u0, kk0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- residual product over this wave's K range, DEC_BATCH steps per load batch
+  struct Batch {
     v4i wv[DEC_BATCH][2], av[DEC_BATCH][MT];
     u32 wsc[DEC_BATCH][2], asc[DEC_BATCH][MT];
+  };
+  auto batch_load = [&](Batch& bt, int s) {
 #pragma unroll
     for (int u = 0; u < DEC_BATCH; u++) {
 #pragma unroll
       for (int tt = 0; tt < 2; tt++) {
-        wv[u][tt] = *reinterpret_cast<const v4i*>(wsrc[tt] + (int64_t)(s + u) * 64);
-        wsc[u][tt] = *reinterpret_cast<const u32*>(wssrc[tt] + (int64_t)(s + u) * 256);
+        bt.wv[u][tt] = *reinterpret_cast<const v4i*>(wsrc[tt] + (int64_t)(s + u) * 1024);
+        bt.wsc[u][tt] = *reinterpret_cast<const u32*>(wssrc[tt] + (int64_t)(s + u) * 256);
       }
 #pragma unroll
       for (int m = 0; m < MT; m++) {
-        av[u][m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)(s + u) * 64);
-        asc[u][m] = *reinterpret_cast<const u32*>(assrc[m] + (int64_t)(s + u) * 256);
+        bt.av[u][m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)(s + u) * 64);
+        bt.asc[u][m] = *reinterpret_cast<const u32*>(assrc[m] + (int64_t)(s + u) * 256);
       }
     }
+  };
+  int s = s0;
+  for (; s + DEC_BATCH <= s1; s += DEC_BATCH) {
+    Batch bt;
+    batch_load(bt, s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s == s0 && up0) up_mma(u0, kk0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < DEC_BATCH; u++) step(wv[u], wsc[u], av[u], asc[u]);
+    for (int u = 0; u < DEC_BATCH; u++) step(bt.wv[u], bt.wsc[u], bt.av[u], bt.asc[u]);
   }
+  if (s == s0 && up0) up_mma(u0, kk0);  // no full batch
   for (; s < s1; s++) {
     v4i wv[2], av[MT];
     u32 wsc[2], asc[MT];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
-      wv[tt] = *reinterpret_cast<const v4i*>(wsrc[tt] + (int64_t)s * 64);
+      wv[tt] = *reinterpret_cast<const v4i*>(wsrc[tt] + (int64_t)s * 1024);
       wsc[tt] = *reinterpret_cast<const u32*>(wssrc[tt] + (int64_t)s * 256);
     }
 #pragma unroll
@@ -105,31 +187,14 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
     }
     step(wv, wsc, av, asc);
   }
-
-  // this wave's share of the up-projection, acc += down[rows, kk..kk+32) . L2^T[cols, kk..kk+32)^T
-  // for kk = 32 w, 32 w + 128, ... (16x16x32 bf16 MFMAs), before the partial tiles are summed
-  if (p.rp > 0) {
-    const T* l2t = reinterpret_cast<const T*>(p.l2t);
-    for (int kk = 32 * wave; kk < p.rp; kk += 128) {
-      v8bf bv[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++) {
-        int col = n0 + 16 * tt + i;
-        col = col < p.npad ? col : p.npad - 1;
-        bv[tt] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)col * p.rp + kk + 8 * g));
-      }
-#pragma unroll
-      for (int m = 0; m < MT; m++) {
-        int row = 16 * m + i;
-        row = row < p.B ? row : p.B - 1;
-        const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, row, kk + 8 * g);
-#pragma unroll
-        for (int tt = 0; tt < 2; tt++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[tt], acc[m][tt], 0, 0, 0);
-      }
-    }
+  // later up-projection rounds (rank above 16 x waves)
+  for (int kk = kk0 + UPW; kk - 4 * g < p.rp; kk += UPW) {
+    UpOps u;
+    up_load(u, kk);
+    up_mma(u, kk);
   }
 
-  // fixed-order sum of the four waves' partial tiles
+  // fixed-order sum of the waves' partial tiles
 #pragma unroll
   for (int m = 0; m < MT; m++)
 #pragma unroll
@@ -144,8 +209,12 @@ __global__ __launch_bounds__(256) void k_gemm_decode_mx(GemmParams p) {
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
       for (int v = 0; v < 4; v++)
-        acc[m][tt][v] = ((red[0][m][tt][lane][v] + red[1][m][tt][lane][v]) + red[2][m][tt][lane][v]) +
-                        red[3][m][tt][lane][v];
+      {
+        float sum = red[0][m][tt][lane][v];
+#pragma unroll
+        for (int w = 1; w < DEC_WAVES; w++) sum += red[w][m][tt][lane][v];
+        acc[m][tt][v] = sum;
+      }
 
   T* y = reinterpret_cast<T*>(p.y);
 #pragma unroll
@@ -170,11 +239,11 @@ hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t str
   if (dtype != SVDQ_BF16 || p.B > 64) return hipErrorNotSupported;
   const int grid = (p.N + DEC_COLS - 1) / DEC_COLS;
   if (p.B <= 16)
-    k_gemm_decode_mx<1><<<grid, 256, 0, stream>>>(p);
+    k_gemm_decode_mx<1, 8><<<grid, 512, 0, stream>>>(p);
   else if (p.B <= 32)
-    k_gemm_decode_mx<2><<<grid, 256, 0, stream>>>(p);
+    k_gemm_decode_mx<2, 8><<<grid, 512, 0, stream>>>(p);
   else
-    k_gemm_decode_mx<4><<<grid, 256, 0, stream>>>(p);
+    k_gemm_decode_mx<4, 4><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

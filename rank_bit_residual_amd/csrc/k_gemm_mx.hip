@@ -17,6 +17,9 @@
 // wave's loads of that stage visible and releases the buffer read in the previous iteration.
 // LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), so
 // the 16-byte reads of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
+// The prepared weight codes are tiled 16 columns x 128 codes per 1 KB, so each wave-wide load
+// of a B stage reads one contiguous kilobyte (the activation codes are row-major: 16 rows x 64
+// bytes per load).
 #include "device_common.h"
 #include "launch.h"
 #include "gemm_pipe.h"
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const int chunk = phys ^ ((row >> 2) & 3);
     int gr = n0 + row;
     gr = gr < p.npad ? gr : p.npad - 1;
-    b_src[j] = p.wcodes + (int64_t)gr * p.ldw + chunk * 16;
+    b_src[j] = p.wcodes + mx_code_tile_offset(gr, p.kq) + chunk * 16;  // tiled: + 1024 per stage
     b_dst[j] = C::A_BYTES + u * 1024;  // u >= B_INSTR lands in the padding after B
   }
   // scales (stage-tiled): waves 0-3 load the 64-row groups 0-3 of the A tile, waves 4-7 those of
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
       __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + st * C::SB), (lds_ptr_t)(base + a_dst[j]), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < C::B_PER_WAVE; j++)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + st * C::SB), (lds_ptr_t)(base + b_dst[j]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + (int64_t)st * 1024), (lds_ptr_t)(base + b_dst[j]), 16, 0, 0);
     if (wave < 4)
       __builtin_amdgcn_global_load_lds((const void*)(sa_src + st * 256), (lds_ptr_t)(base + s_off_a + sw * 256), 4, 0, 0);
     else

@@ -283,10 +283,13 @@ def test_mx_exact_special_case_large_batch():
 
 # ----------------------------------------------------------------------------- decode-batch MXFP4 kernel
 @pytest.mark.parametrize("B,M,N,rank", [
-    (1, 4608, 1000, 32),    # single row; each wave gets 9 K stages (one batch of 8 + a tail)
+    (1, 9216, 1000, 32),    # single row; each of the 8 waves gets 9 K stages (one batch of 8 + a tail)
     (17, 2048, 520, 16),    # two 16-row tiles, the second with one live row
-    (33, 4352, 300, 128),   # four row tiles; uneven K quarters (8 and 9 stages)
+    (33, 4352, 300, 128),   # four row tiles (4 waves); uneven K quarters (8 and 9 stages)
     (64, 1024, 4104, 0),    # full 64 rows, rank 0, N tail inside the last 32-column block
+    (5, 1024, 640, 48),     # K in one chunk: the finished down-projection, no split-K partials
+    (12, 16384, 256, 200),  # 16 split-K partials (more than are prefetched); a second up-projection round
+    (40, 3072, 200, 160),   # four row tiles, three up-projection rounds of 64 rank columns
 ])
 def test_mx_decode_batch_shapes(B, M, N, rank):
     assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]

@@ -52,7 +52,11 @@ def _sections(p):
     Kp, Np, rp = -(-M // 256) * 256, -(-N // 256) * 256, -(-p.rank // 32) * 32
     nib = p.fmt == "mx" or p.bits <= 4
     rb = Kp // 2 if nib else Kp
-    codes = p.section(_lib.SEC_RCODES)[: Np * rb].numpy().reshape(Np, rb)
+    codes = p.section(_lib.SEC_RCODES)[: Np * rb].numpy()
+    if p.fmt == "mx":
+        # 1 KB tiles: [Np/16][Kp/128][16 columns][64 bytes]
+        codes = codes.reshape(Np // 16, Kp // 128, 16, 64).transpose(0, 2, 1, 3)
+    codes = codes.reshape(Np, rb)
     dt = np.float32 if p.dtype == torch.float32 else np.uint16
     E = 16 // np.dtype(dt).itemsize
     # L1^T tiles: [rp/16][Kp/128][32/E K-slices][4 blocks][16 rows][E]
