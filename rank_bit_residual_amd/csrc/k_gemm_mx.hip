@@ -20,6 +20,8 @@
 // The prepared weight codes are tiled 16 columns x 128 codes per 1 KB, so each wave-wide load
 // of a B stage reads one contiguous kilobyte (the activation codes are row-major: 16 rows x 64
 // bytes per load).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "gemm_pipe.h"
@@ -176,42 +178,81 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
                                                                     (int)(sc.a[i] >> sh), 0, (int)(sc.b[j] >> sh));
   };
 
-  // Pipeline: stage s+DIST is issued into the ring, the wave waits until its own loads of
-  // stage s have landed, one barrier publishes every wave's loads of stage s (and guarantees
-  // that the buffer refilled next iteration, last read at stage s-DIST, is no longer read),
-  // then both K slices of stage s are read from LDS and fed to 24 MFMAs. With NS = DIST + 2
-  // buffers a single barrier per stage suffices.
+  // Pipeline: stage s+DIST is issued into the ring at the top of iteration s; slice 1 of stage s
+  // is read from LDS while slice 0's MFMAs run; then the wave waits until its own loads of
+  // stage s+1 have landed, one barrier publishes every wave's loads of that stage, and stage
+  // s+1's scale words and slice-0 operands are read while slice 1's MFMAs of stage s run. No LDS
+  // round trip is exposed between stages, and the MFMAs issued before the barrier keep the
+  // matrix core busy while the waves meet. The barrier of stage s+1 (in iteration s) is also
+  // what makes refilling buffer (s+1+DIST) % NS = (s-1) % NS safe in iteration s+1: every
+  // wave's reads of stage s-1 were consumed by MFMAs issued before it (NS = DIST + 2).
   static_assert(C::NS >= C::DIST + 2, "ring too shallow for the prefetch distance");
+  constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
+  constexpr int NM = C::MT * C::NT;  // MFMAs per slice
+  static_assert(NM > NR, "the interleave schedule assumes more MFMAs than operand reads per slice");
   const int nst = p.kstages;
 #pragma unroll
   for (int s = 0; s < C::DIST; s++)
     if (s < nst) issue(s);
-  Frag f0, f1;
-  for (int s = 0; s < nst; s++) {
-    if (s + C::DIST < nst) issue(s + C::DIST);
-    const int ahead = nst - 1 - s;  // stages issued after s
-    wait_stage<C::LOADS_PER_STAGE, C::DIST + 2>(ahead < C::DIST ? ahead : C::DIST);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+  wait_stage<C::LOADS_PER_STAGE, C::DIST + 2>(nst - 1 < C::DIST - 1 ? nst - 1 : C::DIST - 1);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  Frag fa, fb, f1;
+  Scales sa, sb;
+  read_scales(smem, sa);
+  read_frag(smem, 0, fa);
+
+  // One stage: cur0/scur hold stage s's slice-0 operands and scales; nxt0/snxt receive stage
+  // s+1's unless AHEAD < 0 (the last stage). AHEAD = stages issued after s+1.
+  auto stage = [&](int s, Frag& cur0, Scales& scur, Frag& nxt0, Scales& snxt, auto ahead_c) {
+    constexpr int AHEAD = decltype(ahead_c)::value;
     const uint8_t* base = smem + (s % C::NS) * C::STAGE;
-    Scales sc;
-    read_scales(base, sc);
-    read_frag(base, 0, f0);
     read_frag(base, 1, f1);
-    mma(f0, sc, 0);
-    mma(f1, sc, 1);
-    // Schedule: the scale words and slice 0's operands first, then slice 1's reads one per
-    // MFMA of slice 0, then the remaining MFMAs: one exposed LDS round trip per stage.
-    constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
+    mma(cur0, scur, 0);
+    // slice 1's reads one per slice-0 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
     for (int q = 0; q < NR; q++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::MT * C::NT - NR, 0);
-    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR - 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (AHEAD >= 0) {
+      wait_vmcnt<C::LOADS_PER_STAGE * AHEAD>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const uint8_t* nb = smem + ((s + 1) % C::NS) * C::STAGE;
+      read_scales(nb, snxt);
+      read_frag(nb, 0, nxt0);
+    }
+    mma(f1, scur, 1);
+    // the next stage's scale words and slice-0 reads one per slice-1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int q = 0; q < 2 * NR; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < NM - 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 1 > 2 * NR ? NM - 1 - 2 * NR : 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  typedef std::integral_constant<int, C::DIST - 1> Steady;
+  typedef std::integral_constant<int, 0> LastButOne;
+  typedef std::integral_constant<int, -1> Last;
+
+  // Steady state: every iteration issues stage s + DIST and has DIST - 1 stages in flight after
+  // s + 1; unrolled by two so that the slice-0 operands alternate between fa and fb. nst is
+  // even (Kp is a multiple of 256) and DIST = 2, so the loop leaves exactly the last two stages.
+  static_assert(C::DIST == 2, "the drain below is written for two stages in flight");
+  for (int s = 0; s < nst - C::DIST; s += 2) {
+    issue(s + C::DIST);
+    stage(s, fa, sa, fb, sb, Steady());
+    issue(s + 1 + C::DIST);
+    stage(s + 1, fb, sb, fa, sa, Steady());
   }
+  stage(nst - 2, fa, sa, fb, sb, LastButOne());
+  stage(nst - 1, fb, sb, fa, sa, Last());
 
   // ---- epilogue: up-projection on the matrix cores, one rounding, masked store
   if (p.rp > 0) {
@@ -301,7 +342,7 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
 // Large-batch MXFP4 path for bf16 inputs; returns hipErrorNotSupported when the shape or dtype
 // is not covered, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
-  if (dtype != SVDQ_BF16 || p.B < 256) return hipErrorNotSupported;
+  if (dtype != SVDQ_BF16 || p.B < 256 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
   // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
   // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192).
   const int tiles_m = (p.B + 255) / 256;
