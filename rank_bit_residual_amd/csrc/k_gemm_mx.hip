@@ -191,9 +191,59 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   constexpr int NM = C::MT * C::NT;  // MFMAs per slice
   static_assert(NM > NR, "the interleave schedule assumes more MFMAs than operand reads per slice");
   const int nst = p.kstages;
+
+  // ---- up-projection first: acc = down L2 on bf16 32x32x16 MFMAs. Its first 32 rank columns
+  // are requested before the first stages' DMA and multiplied while those stages land; the
+  // residual product then accumulates on top (one rounding at the end either way).
+  const T* l2t = reinterpret_cast<const T*>(p.l2t);
+  int drow[C::MT], bcol[C::NT];
+#pragma unroll
+  for (int i = 0; i < C::MT; i++) {
+    const int r = m0 + wm * C::TM + 32 * i + l32;
+    drow[i] = r < p.B ? r : p.B - 1;
+  }
+#pragma unroll
+  for (int j = 0; j < C::NT; j++) {
+    const int c = n0 + wn * C::TN + 32 * j + l32;
+    bcol[j] = c < p.npad ? c : p.npad - 1;
+  }
+  struct UpOps {
+    v8bf a[2][C::MT], b[2][C::NT];
+  };
+  auto up_load = [&](UpOps& u, int kk) {  // rank columns [kk, kk + 32), rp a multiple of 32
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+        u.a[h][i] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 16 * h + 8 * g);
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+        u.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 16 * h + 8 * g));
+    }
+  };
+  auto up_mma = [&](const UpOps& u) {
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u.a[h][i], u.b[h][j], acc[i][j], 0, 0, 0);
+  };
+  UpOps u0;
+  if (p.rp > 0) up_load(u0, 0);
 #pragma unroll
   for (int s = 0; s < C::DIST; s++)
     if (s < nst) issue(s);
+  if (p.rp > 0) {
+    up_mma(u0);
+    for (int kk = 32; kk < p.rp; kk += 32) {
+      UpOps u;
+      up_load(u, kk);
+      up_mma(u);
+    }
+  }
+
   wait_stage<C::LOADS_PER_STAGE, C::DIST + 2>(nst - 1 < C::DIST - 1 ? nst - 1 : C::DIST - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -254,51 +304,32 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   stage(nst - 2, fa, sa, fb, sb, LastButOne());
   stage(nst - 1, fb, sb, fa, sa, Last());
 
-  // ---- epilogue: up-projection on the matrix cores, one rounding, masked store
-  if (p.rp > 0) {
-    const T* l2t = reinterpret_cast<const T*>(p.l2t);
-    int drow[C::MT], bcol[C::NT];
-#pragma unroll
-    for (int i = 0; i < C::MT; i++) {
-      const int r = m0 + wm * C::TM + 32 * i + l32;
-      drow[i] = r < p.B ? r : p.B - 1;
-    }
-#pragma unroll
-    for (int j = 0; j < C::NT; j++) {
-      const int c = n0 + wn * C::TN + 32 * j + l32;
-      bcol[j] = c < p.npad ? c : p.npad - 1;
-    }
-    for (int kk = 0; kk < p.rp; kk += 16) {
-      v8bf av[C::MT], bv[C::NT];
-#pragma unroll
-      for (int i = 0; i < C::MT; i++)
-        av[i] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 8 * g);
-#pragma unroll
-      for (int j = 0; j < C::NT; j++)
-        bv[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 8 * g));
-#pragma unroll
-      for (int i = 0; i < C::MT; i++)
-#pragma unroll
-        for (int j = 0; j < C::NT; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  // Stage the rounded tile through the (now idle) LDS ring and write it with 16-byte stores:
-  // lanes hold 4-row x 1-column strips of each 32x32 accumulator, which as direct 2-byte stores
-  // would scatter the output over many partial cache lines.
+  // ---- epilogue: one rounding, staged through the (now idle) LDS ring for 16-byte stores. In a
+  // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Neighbouring lanes
+  // swap one value (DPP quad_perm [1,0,3,2]) so that the even lane holds row 8q + 4g + e,
+  // columns (l32, l32+1) and the odd lane row 8q + 4g + e + 1 of the same two columns
+  // (e = 0, 2): one 4-byte LDS write per pair.
   static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
+  const bool odd = l32 & 1;
   __syncthreads();
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
   for (int i = 0; i < C::MT; i++)
 #pragma unroll
-    for (int j = 0; j < C::NT; j++)
+    for (int j = 0; j < C::NT; j++) {
+      const int c = wn * C::TN + 32 * j + (l32 & ~1);
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int r = wm * C::TM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-        const int c = wn * C::TN + 32 * j + l32;
-        tile[r * BN + c] = DT::from_f32(acc[i][j][v]);
-      }
+      for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float m0v = acc[i][j][4 * q + e], m1v = acc[i][j][4 * q + e + 1];
+          const float send = odd ? m0v : m1v;
+          const float recv = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+          const u32 w = odd ? pack_bf16x2(recv, m1v) : pack_bf16x2(m0v, recv);
+          const int r = wm * C::TM + 32 * i + 8 * q + 4 * g + e + (odd ? 1 : 0);
+          *reinterpret_cast<u32*>(tile + r * BN + c) = w;
+        }
+    }
   __syncthreads();
   T* y = reinterpret_cast<T*>(p.y);
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
