@@ -188,24 +188,40 @@ __device__ inline void unpack_nibbles(u32 w, u32& lo, u32& hi) {
 // MFMAs): read directly, or, when the activation kernel split K over `chunks` blocks, the sum
 // of the f32 partials in chunk order 0, 1, ..., rounded once to bf16 (the same value the
 // unsplit kernel would store).
-__device__ inline v8bf down8_bf16(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
+template <int PF>
+__device__ inline v8bf down8_bf16_pf(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
   if (chunks <= 1)
     return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(down) +
                                                                    (int64_t)row * rp + k));
-  float s[8];
   const float* src = part + (int64_t)row * rp + k;
   const int64_t stride = (int64_t)B * rp;
-  {
-    const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
-    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w; s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  // the first PF chunks are requested together (indices past the last chunk reload the last
+  // one and are not added), the rest one after another; the sum runs in chunk order
+  float4 lo[PF], hi[PF];
+#pragma unroll
+  for (int c = 0; c < PF; c++) {
+    const int cc = c < chunks ? c : chunks - 1;
+    lo[c] = *reinterpret_cast<const float4*>(src + cc * stride);
+    hi[c] = *reinterpret_cast<const float4*>(src + cc * stride + 4);
   }
-  for (int c = 1; c < chunks; c++) {
+  float s[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, hi[0].x, hi[0].y, hi[0].z, hi[0].w};
+#pragma unroll
+  for (int c = 1; c < PF; c++)
+    if (c < chunks) {
+      s[0] += lo[c].x; s[1] += lo[c].y; s[2] += lo[c].z; s[3] += lo[c].w;
+      s[4] += hi[c].x; s[5] += hi[c].y; s[6] += hi[c].z; s[7] += hi[c].w;
+    }
+  for (int c = PF; c < chunks; c++) {
     const float4 a = *reinterpret_cast<const float4*>(src + c * stride), b = *reinterpret_cast<const float4*>(src + c * stride + 4);
     s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w; s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
   }
   return __builtin_bit_cast(v8bf, v4i{(int)pack_bf16x2(s[0], s[1]), (int)pack_bf16x2(s[2], s[3]),
                                       (int)pack_bf16x2(s[4], s[5]), (int)pack_bf16x2(s[6], s[7])});
 }
+__device__ inline v8bf down8_bf16(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
+  return down8_bf16_pf<1>(down, part, chunks, B, rp, row, k);
+}
+
 // One entry down[row][k] as f32 (f32 io): direct, or the ordered sum of the partials.
 __device__ inline float down1_f32(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
   if (chunks <= 1) return reinterpret_cast<const float*>(down)[(int64_t)row * rp + k];

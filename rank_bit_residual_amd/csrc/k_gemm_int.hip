@@ -23,6 +23,8 @@
 // is staged in LDS and written with 16-byte stores.
 // LDS rows are 128 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16-byte reads
 // of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
+#include <type_traits>
+
 #include "device_common.h"
 #include "gemm_pipe.h"
 #include "launch.h"
@@ -38,10 +40,22 @@ constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
 constexpr int STAGE = A_BYTES + B_BYTES;  // 16 KB
 constexpr int A_PER_WAVE = A_BYTES / 1024 / 4, B_PER_WAVE = B_BYTES / 1024 / 4;  // wave-wide 1 KB loads
 constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
-constexpr int NS = 4, DIST = 2;
-constexpr int SMEM = NS * STAGE;          // 64 KB; reused for the partial-tile exchange
+constexpr int DIST = 6, NS = DIST + 2;  // stages in flight (96 KB: covers HBM latency), ring depth
+constexpr int SMEM = NS * STAGE;          // 128 KB; reused for the partial-tile exchange
 static_assert(4 * 4 * 16 * 64 * 4 <= SMEM, "partial tiles must fit the ring");
 }  // namespace gi
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 in order.
+template <int B, int E>
+struct StaticFor {
+  template <class F>
+  __device__ static void run(F&& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>());
+      StaticFor<B + 1, E>::run(f);
+    }
+  }
+};
 
 __device__ inline int swz128(int row, int chunk) { return row * gi::SB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -108,36 +122,99 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0;
 
+  // Pipeline (DIST = 2 stages in flight, NS = DIST + 2 buffers): stage s+DIST is issued at
+  // the top of iteration s; the first 16-code half of stage s is unpacked and fed to the
+  // matrix cores; then the wave waits for its own loads of stage s+1, one barrier publishes
+  // every wave's loads of that stage, and its operands are read from LDS while the second
+  // half's MFMAs of stage s run. The barrier of stage s+1 also guarantees that buffer
+  // (s-1) % NS, refilled in iteration s+1, is no longer read (its operands were consumed by
+  // MFMAs issued before the barrier).
+  static_assert(NS >= DIST + 2 && DIST >= 2, "ring layout assumed below");
   const int nst = p.kstages;
+  const int ch = 2 * wave + g;  // this lane's 16-byte chunk of every stage
+  struct Ops {
+    v4i a[2], b[2];
+  };
+  auto read_stage = [&](int s, Ops& o) {
+    const uint8_t* base = smem + (s % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; i++) o.a[i] = *reinterpret_cast<const v4i*>(base + swz128(32 * i + l32, ch));
+#pragma unroll
+    for (int j = 0; j < 2; j++) o.b[j] = *reinterpret_cast<const v4i*>(base + A_BYTES + swz128(32 * j + l32, ch));
+  };
+  struct Unp {
+    v4i a[2], b[2];
+  };
+  auto unpack = [&](const Ops& o, int h, Unp& u) {  // the chunk's two 16-code halves are two MFMA K steps
+#pragma unroll
+    for (int i = 0; i < 2; i++) u.a[i] = nib16((u32)o.a[i][2 * h], (u32)o.a[i][2 * h + 1]);
+#pragma unroll
+    for (int j = 0; j < 2; j++) u.b[j] = nib16((u32)o.b[j][2 * h], (u32)o.b[j][2 * h + 1]);
+  };
+  auto mfma4 = [&](const Unp& u) {
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(u.a[i], u.b[j], acc[i][j], 0, 0, 0);
+  };
+  // one stage; AHEAD = stages issued after s + 1, or -1 for the last stage. The second half's
+  // unpacking runs under the first half's MFMAs, the next stage's LDS reads under the second's.
+  auto stage = [&](int s, const Ops& cur, Ops& nxt, auto ahead_c) {
+    constexpr int AHEAD = decltype(ahead_c)::value;
+    Unp u0, u1;
+    unpack(cur, 0, u0);
+    mfma4(u0);
+    unpack(cur, 1, u1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (AHEAD >= 0) {
+      wait_vmcnt<LOADS_PER_STAGE * AHEAD>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      read_stage(s + 1, nxt);
+    }
+    mfma4(u1);
+    if constexpr (AHEAD >= 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the four LDS reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  typedef std::integral_constant<int, DIST - 1> Steady;
+
 #pragma unroll
   for (int s = 0; s < DIST; s++)
     if (s < nst) issue(s);
-  const int ch = 2 * wave + g;  // this lane's 16-byte chunk of every stage
-  for (int s = 0; s < nst; s++) {
-    if (s + DIST < nst) issue(s + DIST);
-    const int ahead = nst - 1 - s;
-    wait_stage<LOADS_PER_STAGE, NS>(ahead < DIST ? ahead : DIST);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const uint8_t* base = smem + (s % NS) * STAGE;
-    v4i a4[2], b4[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) a4[i] = *reinterpret_cast<const v4i*>(base + swz128(32 * i + l32, ch));
-#pragma unroll
-    for (int j = 0; j < 2; j++) b4[j] = *reinterpret_cast<const v4i*>(base + A_BYTES + swz128(32 * j + l32, ch));
-#pragma unroll
-    for (int h = 0; h < 2; h++) {  // the chunk's two 16-code halves are two MFMA K steps
-      v4i av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) av[i] = nib16((u32)a4[i][2 * h], (u32)a4[i][2 * h + 1]);
-#pragma unroll
-      for (int j = 0; j < 2; j++) bv[j] = nib16((u32)b4[j][2 * h], (u32)b4[j][2 * h + 1]);
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("" ::: "memory");
+  wait_vmcnt<LOADS_PER_STAGE * (DIST - 1)>();  // nst >= DIST (checked by the launcher)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  Ops oa, ob;
+  read_stage(0, oa);
+  // steady state, unrolled by two so that the operands alternate between oa and ob
+  int s = 0;
+  for (; s + 1 < nst - DIST; s += 2) {
+    issue(s + DIST);
+    stage(s, oa, ob, Steady());
+    issue(s + 1 + DIST);
+    stage(s + 1, ob, oa, Steady());
+  }
+  // the rest: at most one more steady stage, then the last DIST stages (stage nst-DIST+d has
+  // DIST-2-d stages issued after the next one; the last has none to read ahead)
+  auto drain = [&](Ops& x, Ops& y) {
+    StaticFor<0, DIST>::run([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      typedef std::integral_constant<int, DIST - 2 - d> Ahead;
+      if constexpr (d & 1)
+        stage(nst - DIST + d, y, x, Ahead());
+      else
+        stage(nst - DIST + d, x, y, Ahead());
+    });
+  };
+  if (s < nst - DIST) {
+    issue(s + DIST);
+    stage(s, oa, ob, Steady());
+    drain(ob, oa);
+  } else {
+    drain(oa, ob);
   }
 
   // ---- epilogue operands of this wave's quadrant q = (qi, qj), loaded before the exchange so
@@ -155,7 +232,7 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
 #pragma unroll
     for (int r = 0; r < RMAX; r++)
       if (16 * r < p.rp) {
-        ua[r] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g);
+        ua[r] = down8_bf16_pf<4>(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g);
         ub[r] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + 16 * r + 8 * g));
       }
   } else {
@@ -258,7 +335,7 @@ static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
 
 // Per-tensor INT with codes of at most 4 bits (nibbles); other formats fall back.
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
-  if (bits > 4 || p.kstages < 1) return hipErrorNotSupported;
+  if (bits > 4 || p.kstages < gi::DIST) return hipErrorNotSupported;
   if (dtype == SVDQ_BF16) return launch_int4_t<BF16>(p, stream);
   return launch_int4_t<F32>(p, stream);
 }

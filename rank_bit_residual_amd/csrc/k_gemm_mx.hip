@@ -215,7 +215,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     for (int h = 0; h < 2; h++) {
 #pragma unroll
       for (int i = 0; i < C::MT; i++)
-        u.a[h][i] = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 16 * h + 8 * g);
+        u.a[h][i] = down8_bf16_pf<2>(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 16 * h + 8 * g);
 #pragma unroll
       for (int j = 0; j < C::NT; j++)
         u.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 16 * h + 8 * g));

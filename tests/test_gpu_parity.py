@@ -281,6 +281,29 @@ def test_mx_exact_special_case_large_batch():
     assert np.array_equal(_bits(_np(y)), _bits(O.to_dtype(x @ w, "bf16")))
 
 
+# ----------------------------------------------------------------------------- INT4 kernel (K >= 1536)
+def _int_case(B, M, N, rank, dtype, seed):
+    rng = np.random.default_rng(seed)
+    x = O.to_dtype(rng.standard_normal((B, M)) * np.where(rng.random(M) < 0.01, 30.0, 1.0), dtype)
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 3)) @ rng.standard_normal((3, N)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.5)
+    p = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, 4, "int", keep_factors=True)
+    y = R.linear(_g(x, dtype), p)
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "int", 4, dtype)
+    return O.rel_fro(_np(y), ref)
+
+
+@pytest.mark.parametrize("B,M,N,rank,dtype", [
+    (70, 1536, 200, 32, "bf16"),   # K stages = stages in flight: no steady-state iteration
+    (64, 1792, 130, 0, "bf16"),    # 7 stages: one steady iteration (odd), rank 0
+    (130, 2048, 200, 96, "f32"),   # 8 stages, f32 io, up-projection beyond the prefetched steps
+    (256, 2560, 4104, 32, "bf16"), # ragged N across the last 64-column tile
+])
+def test_int4_gemm_shapes(B, M, N, rank, dtype):
+    assert _int_case(B, M, N, rank, dtype, B + M) <= TOL[dtype]
+
+
 # ----------------------------------------------------------------------------- decode-batch MXFP4 kernel
 @pytest.mark.parametrize("B,M,N,rank", [
     (1, 9216, 1000, 32),    # single row; each of the 8 waves gets 9 K stages (one batch of 8 + a tail)
