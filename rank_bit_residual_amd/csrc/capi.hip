@@ -61,6 +61,11 @@ struct Profile {
   std::vector<uint8_t> recorded;  // [call][stage]: both events of the pair were recorded
 };
 Profile g_prof;
+}  // namespace
+
+thread_local GemmEvents g_gemm_events;
+
+namespace {
 
 struct StageTimer {
   hipStream_t s;
@@ -76,6 +81,14 @@ struct StageTimer {
   void end(int stage) const {
     if (on(stage) && hipEventRecord(ev(stage, 1), s) == hipSuccess)
       g_prof.recorded[(size_t)call * SVDQ_NSTAGES + stage] = 1;
+  }
+  // The GEMM stage is one kernel: its events ride on the dispatch (g_gemm_events) instead.
+  void gemm_begin() const {
+    if (on(3)) g_gemm_events = GemmEvents{ev(3, 0), ev(3, 1)};
+  }
+  void gemm_end(hipError_t launched) const {
+    if (on(3) && launched == hipSuccess) g_prof.recorded[(size_t)call * SVDQ_NSTAGES + 3] = 1;
+    g_gemm_events = GemmEvents{};
   }
 };
 
@@ -309,7 +322,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.N = (int)N;
   g.kstages = (int)(d.code_row_bytes() / 128);
   g.npad = (int)d.Np;
-  tm.begin(3);
+  tm.gemm_begin();
   hipError_t ge = hipErrorNotSupported;
   if (fmt == SVDQ_FMT_MX) {
     g.kstages = (int)(d.code_row_bytes() / 64);  // 64-byte stages
@@ -321,8 +334,8 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
     ge = launch_gemm_int4(g, bits, dtype, s);
   }
   if (ge == hipErrorNotSupported) ge = launch_gemm(g, fmt, bits, dtype, s);
+  tm.gemm_end(ge);
   st = hip_status(ge, "residual GEMM launch");
-  tm.end(3);
   return st;
 }
 

@@ -269,8 +269,7 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_gemm<DT, FMT, NIB><<<grid, 256, smem, stream>>>(p);
-  return hipGetLastError();
+  return launch_gemm_kernel(k_gemm<DT, FMT, NIB>, grid, dim3(256), smem, stream, p);
 }
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream) {

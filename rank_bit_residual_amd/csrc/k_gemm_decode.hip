@@ -239,12 +239,11 @@ hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t str
   if (dtype != SVDQ_BF16 || p.B > 64) return hipErrorNotSupported;
   const int grid = (p.N + DEC_COLS - 1) / DEC_COLS;
   if (p.B <= 16)
-    k_gemm_decode_mx<1, 8><<<grid, 512, 0, stream>>>(p);
+    return launch_gemm_kernel(k_gemm_decode_mx<1, 8>, dim3(grid), dim3(512), 0, stream, p);
   else if (p.B <= 32)
-    k_gemm_decode_mx<2, 8><<<grid, 512, 0, stream>>>(p);
+    return launch_gemm_kernel(k_gemm_decode_mx<2, 8>, dim3(grid), dim3(512), 0, stream, p);
   else
-    k_gemm_decode_mx<4, 4><<<grid, 256, 0, stream>>>(p);
-  return hipGetLastError();
+    return launch_gemm_kernel(k_gemm_decode_mx<4, 4>, dim3(grid), dim3(256), 0, stream, p);
 }
 
 }  // namespace svdq

@@ -329,8 +329,7 @@ static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_gemm_int4<DT><<<tiles, 256, gi::SMEM, stream>>>(p);
-  return hipGetLastError();
+  return launch_gemm_kernel(k_gemm_int4<DT>, dim3(tiles), dim3(256), gi::SMEM, stream, p);
 }
 
 // Per-tensor INT with codes of at most 4 bits (nibbles); other formats fall back.

@@ -366,8 +366,7 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_gemm_mx<BF16, BM, BN><<<tiles, 64 * C::NWV, C::SMEM, stream>>>(p);
-  return hipGetLastError();
+  return launch_gemm_kernel(k_gemm_mx<BF16, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
 // Large-batch MXFP4 path for bf16 inputs; returns hipErrorNotSupported when the shape or dtype

@@ -2,6 +2,7 @@
 // Every launcher enqueues on `stream` and returns the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,6 +68,23 @@ hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t 
 // recip[m] = RN(1 / scale[m]) for scale[m] in [2^-90, 2^90], else 0 (the prepared RECIP section).
 hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream_t stream);
 hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream);
+
+// Kernel-timing events for the residual GEMM launch of the current call (svdq_profile_begin):
+// when set, the GEMM launchers pass them to the dispatch itself (hipExtLaunchKernelGGL), so
+// they bracket the kernel's execution and not the queue gap before it.
+struct GemmEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local GemmEvents g_gemm_events;
+
+template <class K, class... Args>
+inline hipError_t launch_gemm_kernel(K kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t stream, Args... args) {
+  if (g_gemm_events.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, g_gemm_events.start, g_gemm_events.stop, 0u, args...);
+  else
+    kernel<<<grid, block, shmem, stream>>>(args...);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
 // Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
