@@ -279,14 +279,10 @@ __device__ __forceinline__ void load_full(const ActParams& p, const T* __restric
   in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * lane);
 }
 
-// Pair Q (elements 2Q, 2Q+1 of the lane's block) of a full bf16 step: X^ = RN_bf16(RN_f32(x/s)).
-// The product t = RN(x * RN(1/s)) lies within 2 f32 ulps of RN_f32(x / s), so RN_bf16(t) is
-// exact unless bf16_fast_risky flags it; flagged elements take the correctly rounded division,
-// with the scale read on that rare path only.
-// Full bf16 steps: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein, with the
-// reciprocal and the scale of each column broadcast from the lane that loaded them (DPP,
-// while the whole wave is active). Branch-free; an overflowing quotient shows up as a bf16 NaN
-// and is replaced by +-infinity afterwards (a wave-uniform branch that real data never takes).
+// Full bf16 steps, exact path: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein,
+// with the reciprocal and the scale of each column broadcast from the lane that loaded them
+// (DPP, while the whole wave is active); an overflowing quotient shows up as a bf16 NaN and is
+// replaced by +-infinity afterwards (a wave-uniform branch that real data never takes).
 // amax16 keeps max |X^| as bf16 bit patterns in two 16-bit lanes (for non-negative values the
 // integer order is the numeric order).
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -303,6 +299,28 @@ __device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& ama
 template <int... Q>
 __device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16) {
   (exact_pair<Q>(in, xb, amax16), ...);
+}
+
+// Pair Q by the fast product: t = RN(x * RN(1/s)) is within 2 f32 ulps of RN_f32(x / s), so
+// RN_bf16(t) is the exact result unless t's low 16 bits lie within 3 of the bf16 rounding
+// midpoint 0x8000. Those low halves are gathered in pairs and their distance to the band
+// kept as a running minimum (packed 16-bit ops); the caller redoes the step exactly when any
+// lane of the wave saw one. (Products that underflow or overflow need no special case: near
+// zero the f32 error is far below the bf16 spacing, past the bf16 range both give inf.)
+template <int Q>
+__device__ __forceinline__ void fast_pair(const FullIn& in, u32* xb, u16x2& amax16, u16x2& band) {
+  const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
+  const float t0 = x0 * row_bcast<Q>(in.y2.x), t1 = x1 * row_bcast<Q>(in.y2.y);
+  const u32 pk = pack_bf16x2(t0, t1);
+  xb[Q] = pk;
+  amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
+  const u32 lows = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);
+  band = __builtin_elementwise_min(band, __builtin_bit_cast(u16x2, lows) + (u16x2){0x8003, 0x8003});
+}
+template <int... Q>
+__device__ __forceinline__ void fast_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16,
+                                           u16x2& band) {
+  (fast_pair<Q>(in, xb, amax16, band), ...);
 }
 
 // Replace bf16 NaNs (quotients that overflowed) by infinity with the sign of x.
@@ -361,7 +379,14 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   if constexpr (FAST) {
     u16x2 amax16 = {0, 0};
     if (__all(in.y2.x != 0.f && in.y2.y != 0.f)) {
-      exact_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16);
+      u16x2 band = {0xFFFF, 0xFFFF};
+      fast_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16, band);
+      // a product near a midpoint, or a NaN, anywhere in the wave: the whole step exactly
+      const bool redo = (band.x < 7 || band.y < 7) || (amax16.x > amax16.y ? amax16.x : amax16.y) > 0x7F80;
+      if (__any(redo)) {
+        amax16 = (u16x2){0, 0};
+        exact_pairs(std::make_integer_sequence<int, 16>{}, in, xb, amax16);
+      }
       if (__any((amax16.x > amax16.y ? amax16.x : amax16.y) > 0x7F80)) {
         // an overflowing quotient somewhere in the wave (never for real activations)
         amax16 = (u16x2){0, 0};
