@@ -107,7 +107,18 @@ def cpu_baseline(wl, x, s, prep, budget_s=10.0):
         done += 2.0 * rows * wl.M * wl.N
     return {"value": done / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"oracle forward_ref on {rows} of {wl.B} rows x {reps} repetitions ({t_total:.1f} s), "
-                      f"float64 numpy BLAS on the host"}
+                      f"float64 numpy BLAS on the host ({_cpu_model()})"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def run(args):
@@ -122,8 +133,11 @@ def run(args):
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     x, w, s = make_inputs(wl)
+    t_prep = time.perf_counter()
     prep = R.prepare(torch.from_numpy(w).to(td), torch.from_numpy(s), wl.rank, wl.bits, wl.fmt, device=dev,
                      keep_factors=not args.no_cpu_baseline)
+    torch.cuda.synchronize()
+    t_prep = time.perf_counter() - t_prep  # host fold + SVD + quantisation + blob copy (one-time)
     B, M, N = wl.B, wl.M, wl.N
     wsb = R.workspace_bytes(B, prep)
     x_g = torch.from_numpy(x).to(td).to(dev)
@@ -150,25 +164,33 @@ def run(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    def stage_times(steps):
+    def stage_times(steps, full=False):
         ms = (ctypes.c_float * (steps * L.NSTAGES))()
         n = ctypes.c_int()
         L.check(lib.svdq_profile_end(ms, steps, ctypes.byref(n)))
         per = np.array(ms[: n.value * L.NSTAGES], dtype=np.float64).reshape(n.value, L.NSTAGES)
+        if full:
+            return per
         return {name: float(per[:, k].mean()) for k, name in enumerate(L.STAGE_NAMES) if per[:, k].any()}
 
-    # ---- timed region: eager launches. The library records one HIP event pair around its
-    # residual-GEMM launch on the call's stream (stage 3 only, to keep host overhead low), so
-    # the roofline's kernel duration comes from the timed calls themselves.
+    def pct(a):
+        return [float(v) for v in np.percentile(np.asarray(a) * 1e3, [10, 50, 90])]
+
+    # ---- timed region: eager launches. The library passes one HIP event pair to the
+    # residual-GEMM dispatch of every EVERY-th call (stage 3 only): the roofline's kernel
+    # duration comes from the timed calls themselves, while an event pair on every call
+    # (about 10 us of host time each) would make the loop host-bound.
     GEMM_STAGE = 3
-    L.check(lib.svdq_profile_begin(args.steps, 1 << GEMM_STAGE))
+    EVERY = 16
+    L.check(lib.svdq_profile_begin_sampled(max(1, args.steps // EVERY + 1), 1 << GEMM_STAGE, EVERY))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t_eager = time.perf_counter() - t0
-    gemm_ms = stage_times(args.steps)["gemm"]
+    gemm_per_call = stage_times(args.steps // EVERY + 1, full=True)[:, GEMM_STAGE]
+    gemm_ms = float(gemm_per_call.mean())
     work = algorithmic(wl, B)
     value = work["flops"] * args.steps / t_eager / 1e12
 
@@ -177,6 +199,15 @@ def run(args):
     for i in range(args.steps):
         step(i)
     stage_ms = stage_times(args.steps)
+
+    # ---- per-call distribution: one HIP event pair around each call on the call's stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in evs]
 
     # ---- HIP-graph replay of the same calls (reported separately, not the headline)
     graph = None
@@ -231,6 +262,10 @@ def run(args):
                    "io_dtype": wl.dtype, "rotating_copies": copies},
         "roofline": roof,
         "call_gbs": work["call_bytes"] / (t_eager / args.steps) / 1e9,
+        "call_us_p10_p50_p90": pct(call_ms),
+        "gemm_us_p10_p50_p90": pct(gemm_per_call),
+        "gemm_timed_calls": int(len(gemm_per_call)),
+        "host_prepare_s": t_prep,
         "kernels_ms": stage_ms,
         "graph": graph,
     }

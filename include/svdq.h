@@ -231,7 +231,11 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
  * Kernel timing (profiling aid; not on any page). Between svdq_profile_begin and
  * svdq_profile_end, each svdq_linear call records a HIP event pair around every kernel it
  * launches whose stage bit is set in stage_mask, on the call's stream, for up to max_calls
- * calls. Stages: 0 = per-tensor max pre-pass (INT), 1 = smooth+quantise+down-projection,
+ * calls (svdq_profile_begin_sampled: only every `every`-th call, counting from the first
+ * after the session opens, is recorded, up to max_calls recorded calls). The residual GEMM
+ * (stage 3) is a single kernel and its pair is carried by the dispatch itself, so it brackets
+ * the kernel's execution; the other stages' pairs bracket their launches on the stream.
+ * Stages: 0 = per-tensor max pre-pass (INT), 1 = smooth+quantise+down-projection,
  * 2 = reserved (no kernel; split-K partials of the down-projection are summed in the GEMM
  * epilogue), 3 = residual GEMM + epilogue; a stage that did not run or was not selected
  * reads 0. Each event pair costs host time per call, so a throughput
@@ -245,6 +249,7 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
  * ------------------------------------------------------------------------------------ */
 #define SVDQ_NSTAGES 4
 int svdq_profile_begin(int max_calls, unsigned stage_mask);
+int svdq_profile_begin_sampled(int max_calls, unsigned stage_mask, int every); /* EINVAL if every < 1 */
 int svdq_profile_end(float* ms, int cap, int* n_calls);
 
 #ifdef __cplusplus

@@ -31,6 +31,7 @@ SIGNATURES = {
     "svdq_quantize_activations": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                                           c_i64, c_vp, c_vp, c_sz, c_vp]),
     "svdq_profile_begin": (c_int, [c_int, ctypes.c_uint]),
+    "svdq_profile_begin_sampled": (c_int, [c_int, ctypes.c_uint, c_int]),
     "svdq_profile_end": (c_int, [ctypes.POINTER(ctypes.c_float), c_int, ctypes.POINTER(c_int)]),
 }
 NSTAGES = 4

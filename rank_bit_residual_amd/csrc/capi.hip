@@ -55,7 +55,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // Kernel-timing session (svdq_profile_begin / svdq_profile_end).
 struct Profile {
   bool open = false;
-  int max_calls = 0, calls = 0;
+  int max_calls = 0, calls = 0;  // recorded calls: capacity and count
+  int every = 1, seen = 0;        // record calls seen % every == 0
   unsigned mask = 0;              // stages that record events
   std::vector<hipEvent_t> ev;     // [call][stage][begin, end]
   std::vector<uint8_t> recorded;  // [call][stage]: both events of the pair were recorded
@@ -71,7 +72,7 @@ struct StageTimer {
   hipStream_t s;
   int call = -1;
   explicit StageTimer(hipStream_t s_) : s(s_) {
-    if (g_prof.open && g_prof.calls < g_prof.max_calls) call = g_prof.calls++;
+    if (g_prof.open && g_prof.calls < g_prof.max_calls && g_prof.seen++ % g_prof.every == 0) call = g_prof.calls++;
   }
   hipEvent_t ev(int stage, int which) const { return g_prof.ev[((size_t)call * SVDQ_NSTAGES + stage) * 2 + which]; }
   bool on(int stage) const { return call >= 0 && ((g_prof.mask >> stage) & 1u); }
@@ -339,9 +340,12 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   return st;
 }
 
-int svdq_profile_begin(int max_calls, unsigned stage_mask) {
+int svdq_profile_begin(int max_calls, unsigned stage_mask) { return svdq_profile_begin_sampled(max_calls, stage_mask, 1); }
+
+int svdq_profile_begin_sampled(int max_calls, unsigned stage_mask, int every) {
   clear_error();
   if (max_calls < 1) return set_error(SVDQ_EINVAL, "max_calls must be >= 1");
+  if (every < 1) return set_error(SVDQ_EINVAL, "every must be >= 1");
   if (stage_mask == 0 || (stage_mask >> SVDQ_NSTAGES)) return set_error(SVDQ_EINVAL, "stage_mask must select stages 0..3");
   if (g_prof.open) return set_error(SVDQ_EINVAL, "a profiling session is already open");
   g_prof.ev.assign((size_t)max_calls * SVDQ_NSTAGES * 2, nullptr);
@@ -359,6 +363,8 @@ int svdq_profile_begin(int max_calls, unsigned stage_mask) {
   g_prof.mask = stage_mask;
   g_prof.max_calls = max_calls;
   g_prof.calls = 0;
+  g_prof.every = every;
+  g_prof.seen = 0;
   return SVDQ_OK;
 }
 

@@ -52,5 +52,7 @@ def test_host_calls_report_errors_without_a_gpu():
     assert lib.svdq_profile_begin(4, 0) == _lib.SVDQ_EINVAL
     assert lib.svdq_profile_begin(4, 16) == _lib.SVDQ_EINVAL
     assert b"stage_mask" in lib.svdq_last_error()
+    assert lib.svdq_profile_begin_sampled(4, 8, 0) == _lib.SVDQ_EINVAL
+    assert b"every" in lib.svdq_last_error()
     n = ctypes.c_int()
     assert lib.svdq_profile_end(None, 0, ctypes.byref(n)) == _lib.SVDQ_EINVAL  # no open session
