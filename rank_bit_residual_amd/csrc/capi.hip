@@ -17,7 +17,9 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   LaunchPlan p;
   p.B = B;
   p.row_blocks = (int)ceil_div(B, 16);
-  p.r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, 64) : 1;
+  // 16-wide rank chunks when 64-wide ones would leave most of the chip idle (decode batches)
+  p.rchunk = (d.rp > 0 && (int64_t)p.row_blocks * ceil_div(d.rp, 64) < 256) ? 16 : 64;
+  p.r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, p.rchunk) : 1;
   // Split K across blocks only when rows x low-rank chunks give fewer than ~256 blocks, and
   // never below one 128-wide step per wave of a block (8 waves: 1024 K per chunk).
   const int64_t per = (int64_t)p.row_blocks * p.r_chunks;
@@ -232,7 +234,7 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
   p.k_chunks = pl.k_chunks;
   p.k_chunk_len = pl.k_chunk_len;
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
-  return hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, 1, s), "quantize_activations launch");
+  return hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, 1, 64, s), "quantize_activations launch");
 }
 
 int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob, int64_t N, int64_t rank, int fmt,
@@ -297,7 +299,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   p.k_chunk_len = pl.k_chunk_len;
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
   tm.begin(1);
-  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, s), "activation quantise launch")))
+  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, pl.rchunk, s), "activation quantise launch")))
     return st;
   tm.end(1);
   // (c): residual GEMM + epilogue

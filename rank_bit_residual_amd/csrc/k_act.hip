@@ -197,7 +197,9 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
 // of the step's loads are independent and issue together); only the tail step and the zero
 // padding up to Kp take the guarded body.
 constexpr int ACT_WAVES = 8;
-constexpr int ACT_RCHUNK = 64;
+// Low-rank columns per block (RC, a template parameter of the kernel): 64, or 16 when rows x
+// rank chunks would give too few blocks (decode-sized batches); the 16-wide form repeats the
+// smoothing of its K range for each rank chunk, which is cheap next to the parallelism won.
 
 template <class DT>
 __device__ inline void load_row32(const typename DT::T* __restrict__ xrow, int k, int M, bool vec_ok, u32* raw) {
@@ -333,7 +335,7 @@ __device__ __forceinline__ u32 nan_to_inf_pair(u32 pk, u32 raw) {
 
 // One 128-wide K step of one wave (see the kernel comment). FULL bf16 steps take their x and
 // reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
-template <class DT, int FMT, bool NIB, bool FULL>
+template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
                                          int k0, v4f* acc, const FullIn& in) {
   typedef typename DT::T T;
@@ -359,7 +361,7 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
     load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
   }
   // B operands of the down-projection for this step
-  constexpr int NB = ACT_RCHUNK / 16;
+  constexpr int NB = RC / 16;
   // (bf16: loaded with the step's other loads; f32 loads them at the MFMAs to save registers)
   v4i bw[NB][4];
   if (DT::is_bf16 && L.nbl > 0) {
@@ -543,11 +545,11 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   }
 }
 
-template <class DT, int FMT, bool NIB>
+template <class DT, int FMT, bool NIB, int RC>
 __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   typedef typename DT::T T;
   constexpr int NW = ACT_WAVES;
-  __shared__ float red[NW][16][ACT_RCHUNK];
+  __shared__ float red[NW][16][RC];
   ActLane L;
   L.lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -558,8 +560,8 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   const int bl = L.b < p.B ? L.b : p.B - 1;
   const int kbeg = blockIdx.y * p.k_chunk_len;
   const int kend = kbeg + p.k_chunk_len < p.Kp ? kbeg + p.k_chunk_len : p.Kp;
-  L.rbase = blockIdx.z * ACT_RCHUNK;
-  L.nbl = p.rp > L.rbase ? ((p.rp - L.rbase) >= ACT_RCHUNK ? ACT_RCHUNK / 16 : (p.rp - L.rbase) / 16) : 0;
+  L.rbase = blockIdx.z * RC;
+  L.nbl = p.rp > L.rbase ? ((p.rp - L.rbase) >= RC ? RC / 16 : (p.rp - L.rbase) / 16) : 0;
   L.do_codes = blockIdx.z == 0 && p.codes != nullptr;
   const T* __restrict__ xrow = reinterpret_cast<const T*>(p.x) + (int64_t)bl * p.ldx;
 
@@ -582,9 +584,9 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
     if (p.sx_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *p.sx_out = L.sx;
   }
 
-  v4f acc[ACT_RCHUNK / 16];
+  v4f acc[RC / 16];
 #pragma unroll
-  for (int n = 0; n < ACT_RCHUNK / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < RC / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // full steps first (k0 ascending), then the tail and padding; bf16 full steps load the next
   // step's x and reciprocals before computing the current one
@@ -599,21 +601,21 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
         const bool more = kn < kend && kn + 128 <= kfull;
         FullIn nxt;
         if (more) load_full(p, xrow, L.lane, L.g, kn, nxt);
-        act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc, cur);
+        act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur);
         k0 = kn;
         if (!more) break;
         cur = nxt;
       }
     }
   } else {
-    for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true>(p, xrow, L, k0, acc, cur);
+    for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur);
   }
-  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false>(p, xrow, L, k0, acc, cur);
+  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false, RC>(p, xrow, L, k0, acc, cur);
 
   if (L.nbl > 0) {
     // fixed-order sum of the waves' partial down-projections
 #pragma unroll
-    for (int n = 0; n < ACT_RCHUNK / 16; n++)
+    for (int n = 0; n < RC / 16; n++)
       if (n < L.nbl)
 #pragma unroll
         for (int v = 0; v < 4; v++) red[wave][4 * L.g + v][16 * n + L.i] = acc[n][v];
@@ -721,12 +723,19 @@ hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream) {
+hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, int rchunk,
+                            hipStream_t stream) {
   const dim3 grid(row_blocks, p.k_chunks, r_chunks);
   const int threads = 64 * ACT_WAVES;
   const bool nib = fmt == SVDQ_FMT_MX || p.bits <= 4;
-#define SVDQ_ACT(DT, FMT, NIB) k_act_quant<DT, FMT, NIB><<<grid, threads, 0, stream>>>(p)
-  if (!p.recip) return hipErrorInvalidValue;
+#define SVDQ_ACT(DT, FMT, NIB)                                       \
+  do {                                                                \
+    if (rchunk == 16)                                                 \
+      k_act_quant<DT, FMT, NIB, 16><<<grid, threads, 0, stream>>>(p); \
+    else                                                              \
+      k_act_quant<DT, FMT, NIB, 64><<<grid, threads, 0, stream>>>(p); \
+  } while (0)
+  if (!p.recip || (rchunk != 16 && rchunk != 64)) return hipErrorInvalidValue;
   if (dtype == SVDQ_BF16) {
     if (fmt == SVDQ_FMT_MX)
       SVDQ_ACT(BF16, SVDQ_FMT_MX, true);

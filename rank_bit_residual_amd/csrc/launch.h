@@ -67,7 +67,9 @@ hipError_t launch_fake_quant(const void* z, int64_t rows, int64_t cols, int64_t 
                              const float* part, int nparts, void* out, int64_t ldo, float* s_out, hipStream_t stream);
 // recip[m] = RN(1 / scale[m]) for scale[m] in [2^-90, 2^90], else 0 (the prepared RECIP section).
 hipError_t launch_reciprocals(const float* scale, int M, float* recip, hipStream_t stream);
-hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, hipStream_t stream);
+// grid (row_blocks, p.k_chunks, r_chunks) of blocks covering rchunk (16 or 64) low-rank columns each
+hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_blocks, int r_chunks, int rchunk,
+                            hipStream_t stream);
 
 // Kernel-timing events for the residual GEMM launch of the current call (svdq_profile_begin):
 // when set, the GEMM launchers pass them to the dispatch itself (hipExtLaunchKernelGGL), so
