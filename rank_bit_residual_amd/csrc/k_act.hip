@@ -333,16 +333,27 @@ __device__ __forceinline__ u32 nan_to_inf_pair(u32 pk, u32 raw) {
   return r;
 }
 
-// One 128-wide K step of one wave (see the kernel comment). FULL bf16 steps take their x and
-// reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
+// State a step carries from its smoothing half to its codes + down-projection half: X^ as
+// stored (bf16 pairs or f32 bits), max |X^| of the lane's block, and (bf16) the step's L1^T
+// operands.
+template <class DT, int RC>
+struct StepState {
+  u32 xb[DT::is_bf16 ? 16 : 32];
+  float amax;
+  v4i bw[RC / 16][4];
+};
+
+// First half of a step: loads, X^ = D(x / scale) and its block maximum.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
-__device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                         int k0, v4f* acc, const FullIn& in) {
+__device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
+                                           int k0, const FullIn& in, StepState<DT, RC>& st) {
   typedef typename DT::T T;
   constexpr int RW = DT::is_bf16 ? 16 : 32;
   constexpr bool FAST = DT::is_bf16 && FULL;
   const int k = k0 + 32 * L.g;
   const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
+  u32* xb = st.xb;
+  auto& bw = st.bw;
 
   u32 raw[RW];
   float s32[32], y32[32];
@@ -363,7 +374,6 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   // B operands of the down-projection for this step
   constexpr int NB = RC / 16;
   // (bf16: loaded with the step's other loads; f32 loads them at the MFMAs to save registers)
-  v4i bw[NB][4];
   if (DT::is_bf16 && L.nbl > 0) {
 #pragma unroll
     for (int n = 0; n < NB; n++)
@@ -376,7 +386,6 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
 
   // X^ = D(x / scale); xb: X^ as stored (bf16 pairs or f32 bits); amax: max |X^| before the
   // final rounding to the dtype (rounding is monotone, so it rounds to max |X^|).
-  u32 xb[RW];
   float amax = 0.f;
   if constexpr (FAST) {
     u16x2 amax16 = {0, 0};
@@ -445,6 +454,21 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
       }
     }
   }
+  st.amax = amax;
+}
+
+// Second half of a step: activation codes (block or per-tensor scale) and the step's share of
+// down = X^ L1 on the matrix cores.
+template <class DT, int FMT, bool NIB, int RC>
+__device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L, int k0, v4f* acc,
+                                           const StepState<DT, RC>& st) {
+  typedef typename DT::T T;
+  constexpr int NB = RC / 16;
+  const int k = k0 + 32 * L.g;
+  const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
+  const u32* xb = st.xb;
+  const auto& bw = st.bw;
+  const float amax = st.amax;
   auto val = [&](int j) -> float {
     if constexpr (DT::is_bf16)
       return (j & 1) ? __uint_as_float(xb[j / 2] & 0xFFFF0000u) : __uint_as_float(xb[j / 2] << 16);
@@ -543,6 +567,17 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
         }
     }
   }
+}
+
+
+// One 128-wide K step of one wave (see the kernel comment). FULL bf16 steps take their x and
+// reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
+template <class DT, int FMT, bool NIB, bool FULL, int RC>
+__device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
+                                         int k0, v4f* acc, const FullIn& in) {
+  StepState<DT, RC> st;
+  act_smooth<DT, FMT, NIB, FULL, RC>(p, xrow, L, k0, in, st);
+  act_finish<DT, FMT, NIB, RC>(p, L, k0, acc, st);
 }
 
 template <class DT, int FMT, bool NIB, int RC>

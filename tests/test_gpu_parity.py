@@ -128,6 +128,41 @@ def test_activation_codes_bit_exact_workloads(cid):
     _check_codes(x, s, wl.fmt, wl.bits, wl.dtype)
 
 
+def test_int_linear_graph_replay_matches_eager():
+    """The INT path (max pre-pass, activation kernel, INT4 GEMM) captured in a HIP graph:
+    every replay must equal the eager result."""
+    rng = np.random.default_rng(17)
+    B, M, N = 64, 2048, 512
+    x = O.to_dtype(rng.standard_normal((B, M)), "bf16")
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)), "bf16")
+    from workloads import smoothing_scale
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(smoothing_scale(x, w, 0.5)), 32, 4, "int")
+    xg = _g(x, "bf16")
+    want = R.linear(xg, p)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(dev())
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        out = R.linear(xg, p)  # warm-up on the capture stream (allocates the workspace)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            out = R.linear(xg, p)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("B,M,N", [(4200, 1536, 256), (300, 4096, 200)])
+def test_int_linear_batch_routes(B, M, N):
+    """B = 4200: 263 row blocks, no K split, two K steps per wave of the activation kernel;
+    B = 300: K split into four chunks whose partials the INT4 GEMM sums."""
+    assert _int_case(B, M, N, 32, "bf16", B) <= TOL["bf16"]
+
+
 def test_activation_codes_double_rounding_boundaries():
     x, s = double_boundary_case()
     _check_codes(x, s, "mx", 4, "bf16")
