@@ -17,6 +17,7 @@ has more than 2*24+2 significand bits), so f32(a / b) below is IEEE division.
 """
 from __future__ import annotations
 
+import math
 import struct
 
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
@@ -131,3 +132,21 @@ def forward(x, scale, left, right, residual, fmt, bits, dtype):
         act, wgt = act_rows, wgt_cols
     y = [[low[b][n] + res[b][n] for n in range(N)] for b in range(B)]
     return y, act, wgt
+
+
+def calibrate_scale(x, weight, alpha):
+    """Brute force of the calibrated smoothing scale: column maxima of |x| and row maxima of
+    |W| by plain loops, then max|x|^alpha / max|W|^(1-alpha) with math.pow, rounded to f32;
+    1 where a maximum is 0."""
+    B, M = len(x), len(x[0])
+    N = len(weight[0])
+    out = []
+    for m in range(M):
+        ax = 0.0
+        for b in range(B):
+            ax = max(ax, abs(float(x[b][m])))
+        aw = 0.0
+        for n in range(N):
+            aw = max(aw, abs(float(weight[m][n])))
+        out.append(1.0 if ax == 0.0 or aw == 0.0 else f32(math.pow(ax, alpha) / math.pow(aw, 1.0 - alpha)))
+    return out

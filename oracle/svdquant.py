@@ -292,6 +292,30 @@ def svdquant_linear(x, weight, scale, rank: int, bits: int = 4):
     return to_dtype(y, dtype)
 
 
+# --------------------------------------------------------------------------- scale calibration
+def calibrate_scale(x, weight, alpha: float) -> np.ndarray:
+    """Per-input-channel smoothing scale from a calibration batch, the step before the path:
+    s[m] = max_b |x[b,m]|^alpha / max_n |W[m,n]|^(1 - alpha), evaluated in float64 and
+    rounded once to float32, with s[m] = 1 where either maximum is 0 (so the scale stays a
+    valid positive divisor). [P4] step 2 names the migration strength iter_smooth.alpha
+    (0.25 in its diffusion example); the closed form is the reading of the design notes (R16),
+    the same one the synthetic workloads use for their input scales.
+
+    x: [B, M] calibration activations, weight: [M, N]; alpha in [0, 1]."""
+    x = np.asarray(x)
+    weight = np.asarray(weight)
+    if x.ndim != 2 or weight.ndim != 2 or x.shape[1] != weight.shape[0] or x.size == 0 or weight.size == 0:
+        raise ValueError("x [B,M] and weight [M,N] must be nonempty with matching M")
+    if not (0.0 <= alpha <= 1.0):
+        raise ValueError("alpha must be in [0, 1]")
+    ax = np.max(np.abs(x.astype(np.float64)), axis=0)
+    aw = np.max(np.abs(weight.astype(np.float64)), axis=1)
+    s = np.ones(x.shape[1], np.float64)
+    ok = (ax > 0) & (aw > 0)
+    s[ok] = np.power(ax[ok], alpha) / np.power(aw[ok], 1.0 - alpha)
+    return s.astype(np.float32)
+
+
 def rel_fro(y, ref) -> float:
     """Relative Frobenius error ||y - ref||_F / ||ref||_F (float64)."""
     y = np.asarray(y, np.float64)

@@ -383,3 +383,45 @@ def test_forward_full_rank_recovers_product(fmt):
     left, right, res = O.split_weight(ws, 48, "f32")
     y = O.forward_ref(x, s, left, right, res, fmt, 4, "f32")
     assert O.rel_fro(y, x.astype(np.float64) @ w.astype(np.float64)) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- scale calibration
+def test_calibrate_scale_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "calib_worked.json")))
+    x, w = np.array(g["x"], np.float32), np.array(g["w"], np.float32)
+    for c in g["cases"]:
+        got = O.calibrate_scale(x, w, c["alpha"])
+        assert got.dtype == np.float32 and np.array_equal(got, np.array(c["scale"], np.float32)), c
+
+
+def test_calibrate_scale_against_loops_and_invariants():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_t(3, (9, 12)) * 10.0 ** rng.integers(-3, 3, (9, 12))).astype(np.float32)
+    w = (rng.standard_normal((12, 7)) * 10.0 ** rng.integers(-2, 2, (12, 7))).astype(np.float32)
+    x[:, 3] = 0.0
+    w[5] = 0.0
+    for alpha in (0.0, 0.25, 0.5, 0.9, 1.0):
+        got = O.calibrate_scale(x, w, alpha)
+        assert np.array_equal(got, np.array(loops.calibrate_scale(x.tolist(), w.tolist(), alpha), np.float32))
+        assert got[3] == 1.0 and got[5] == 1.0 and np.all(got > 0)
+    # alpha = 1: the column maximum itself; scaling x by 4 doubles the scale at alpha = 0.5
+    # and leaves it at alpha = 0
+    ax = np.max(np.abs(x), axis=0)
+    ok = (ax > 0) & (np.max(np.abs(w), axis=1) > 0)
+    assert np.array_equal(O.calibrate_scale(x, w, 1.0)[ok], ax[ok])
+    assert np.array_equal(O.calibrate_scale(4 * x, w, 0.5), np.where(ok, 2, 1) * O.calibrate_scale(x, w, 0.5))
+    assert np.array_equal(O.calibrate_scale(4 * x, w, 0.0), O.calibrate_scale(x, w, 0.0))
+    # a smoothing with the calibrated scale balances the channel maxima: max|x/s| and
+    # max|s W| agree up to rounding where alpha = 0.5
+    s = O.calibrate_scale(x, w, 0.5).astype(np.float64)
+    mx = np.max(np.abs(x / s), axis=0)
+    mw = np.max(np.abs(s[:, None] * w), axis=1)
+    assert np.allclose(mx[ok], mw[ok], rtol=1e-6)
+
+
+@pytest.mark.parametrize("alpha", [-0.1, 1.5])
+def test_calibrate_scale_rejects(alpha):
+    with pytest.raises(ValueError):
+        O.calibrate_scale(np.ones((2, 3), np.float32), np.ones((3, 2), np.float32), alpha)
+    with pytest.raises(ValueError):
+        O.calibrate_scale(np.ones((2, 3), np.float32), np.ones((4, 2), np.float32), 0.5)
