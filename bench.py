@@ -274,6 +274,81 @@ def run(args):
     print(json.dumps(out), flush=True)
 
 
+def run_calibrate(args):
+    """Smoothing-scale calibration (the step before the operator's path) on a workload's x and
+    W: svdq_calibrate_scale timed over rotating copies of (x, W), GB/s of its algorithmic bytes
+    (x + W + the float32 scale) against the HBM peak, and the oracle on the host beside it."""
+    import numpy as np
+    import torch
+
+    from rank_bit_residual_amd import _lib as L
+    from workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    alpha = wl.alpha
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x, w, _ = make_inputs(wl)
+    B, M, N = wl.B, wl.M, wl.N
+    x_g = torch.from_numpy(x).to(td).to(dev)
+    w_g = torch.from_numpy(w).to(td).to(dev)
+    e = x_g.element_size()
+    nbytes = (B * M + M * N) * e + 4 * M
+    copies = max(2, math.ceil(args.rotate_mb * 2**20 / nbytes))
+    xs = [x_g.clone() for _ in range(copies)]
+    wss = [w_g.clone() for _ in range(copies)]
+    lib = L.load()
+    wsb = ctypes.c_size_t()
+    L.check(lib.svdq_calibrate_workspace_bytes(B, M, ctypes.byref(wsb)))
+    work = torch.empty(wsb.value, dtype=torch.uint8, device=dev)
+    out = torch.empty(M, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dt = L.SVDQ_BF16 if wl.dtype == "bf16" else L.SVDQ_F32
+
+    def step(i):
+        L.check(lib.svdq_calibrate_scale(ctypes.c_void_p(xs[i % copies].data_ptr()), B, M, M,
+                                         ctypes.c_void_p(wss[i % copies].data_ptr()), N, N, dt, alpha,
+                                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(work.data_ptr()),
+                                         wsb.value, ctypes.c_void_p(stream.cuda_stream)))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    gbs = nbytes / (call_ms.mean() / 1e3) / 1e9
+    res = {"metric": "svdq_calibrate_scale GB/s (x + W + scale) and % of HBM roofline, 1xMI355X", "value": gbs,
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": t_wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f64", "data": "synthetic",
+           "config": {"workload": wl.name + "_calibration", "B": B, "M": M, "N": N, "alpha": alpha,
+                      "io_dtype": wl.dtype, "rotating_copies": copies},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK["hbm"], "unit": "GB/s",
+                        "frac": gbs / PEAK["hbm"], "traffic": None, "kernel": "k_calib_colmax + k_calib_finish",
+                        "avg_ms": float(call_ms.mean()), "algorithmic_bytes": nbytes},
+           "call_us_p10_p50_p90": [float(v) for v in np.percentile(call_ms * 1e3, [10, 50, 90])]}
+    if not args.no_cpu_baseline:
+        from oracle import svdquant as O
+
+        reps, t_total = 0, 0.0
+        while t_total < 10.0 and reps < 1000:
+            t1 = time.perf_counter()
+            O.calibrate_scale(x, w, alpha)
+            t_total += time.perf_counter() - t1
+            reps += 1
+        res["cpu_baseline"] = {"value": nbytes * reps / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle calibrate_scale on the whole workload x {reps} repetitions "
+                                         f"({t_total:.1f} s), numpy on the host ({_cpu_model()})"}
+    print(json.dumps(res), flush=True)
+
+
 def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, wl, command):
     """Per-dispatch HBM bytes of the residual GEMM from rocprofv3 counter CSVs (FETCH_SIZE and
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain
@@ -317,6 +392,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_BYTES"))
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time the smoothing-scale calibration on the workload's x and W instead of the operator")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -342,7 +419,10 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    run(args)
+    if args.calibrate:
+        run_calibrate(args)
+    else:
+        run(args)
     return 0
 
 

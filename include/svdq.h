@@ -228,6 +228,25 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
                               void* workspace, size_t workspace_bytes, svdq_stream_t stream);
 
 /* --------------------------------------------------------------------------------------
+ * svdq_calibrate_scale — the smoothing scale from a calibration batch (the step before
+ * the path): scale_out[m] = max_b |x[b,m]|^alpha / max_n |W[m,n]|^(1-alpha), computed in
+ * binary64 and rounded once to float32, and 1 where either maximum is 0. [MS] step 2 names
+ * the migration strength iter_smooth.alpha (0.25 in its diffusion example) but prints no
+ * formula; this closed form (the SmoothQuant-style balance of the two channel maxima) is the
+ * library's reading of it.
+ *   x: device [B, M] of dtype, row stride ldx >= M (elements); weight: device [M, N], row
+ *   stride ldw >= N; scale_out: device float32 [M] (written); workspace: device, 256-byte
+ *   aligned, at least svdq_calibrate_workspace_bytes(B, M) bytes, holding the per-block
+ *   column maxima (no zeroing needed). Two kernels on `stream`; asynchronous.
+ *   Errors: EDTYPE; EINVAL for NULL buffers, empty shapes, short strides, alpha outside
+ *   [0, 1] (or NaN), a small or misaligned workspace, misaligned buffers; EHIP.
+ * ------------------------------------------------------------------------------------ */
+int svdq_calibrate_workspace_bytes(int64_t B, int64_t M, size_t* bytes_out);
+int svdq_calibrate_scale(const void* x, int64_t B, int64_t M, int64_t ldx, const void* weight, int64_t N,
+                         int64_t ldw, int dtype, double alpha, float* scale_out, void* workspace,
+                         size_t workspace_bytes, svdq_stream_t stream);
+
+/* --------------------------------------------------------------------------------------
  * Kernel timing (profiling aid; not on any page). Between svdq_profile_begin and
  * svdq_profile_end, each svdq_linear call records a HIP event pair around every kernel it
  * launches whose stage bit is set in stage_mask, on the call's stream, for up to max_calls

@@ -107,6 +107,27 @@ def smooth_inputs(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor):
     return xs, ws
 
 
+def calibrate_scale(x: torch.Tensor, weight: torch.Tensor, alpha: float) -> torch.Tensor:
+    """Smoothing scale from a calibration batch on the device: float32 [M] with
+    max|x[:,m]|^alpha / max|W[m,:]|^(1-alpha) (1 where a maximum is 0)."""
+    _require_gpu(x, weight)
+    _check_same(x, weight)
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[0]:
+        raise ValueError("x [B,M] and weight [M,N] must share M")
+    lib = L.load()
+    xc = x if x.stride(1) == 1 else x.contiguous()
+    wc = weight if weight.stride(1) == 1 else weight.contiguous()
+    B, M = xc.shape
+    N = wc.shape[1]
+    wsb = ctypes.c_size_t()
+    L.check(lib.svdq_calibrate_workspace_bytes(B, M, ctypes.byref(wsb)))
+    work = torch.empty(wsb.value, dtype=torch.uint8, device=x.device)
+    out = torch.empty(M, dtype=torch.float32, device=x.device)
+    L.check(lib.svdq_calibrate_scale(_ptr(xc), B, M, xc.stride(0), _ptr(wc), N, wc.stride(0), _dtype_code(x),
+                                     float(alpha), _ptr(out), _ptr(work), wsb.value, _stream(x)))
+    return out
+
+
 def split_weight(weight: torch.Tensor, rank: int):
     """Return (left [M,r], right [r,N], residual [M,N]) of the library's truncated SVD.
 

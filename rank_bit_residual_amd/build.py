@@ -28,6 +28,7 @@ HIP_SOURCES = {
     "k_gemm_mx.hip": [],
     "k_gemm_decode.hip": [],
     "k_gemm_int.hip": [],
+    "k_calib.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

@@ -155,6 +155,36 @@ int svdq_smooth_inputs(const void* x, int64_t B, int64_t M, int64_t sxb, int64_t
                     "smooth_inputs launch");
 }
 
+int svdq_calibrate_workspace_bytes(int64_t B, int64_t M, size_t* bytes_out) {
+  clear_error();
+  if (!bytes_out) return set_error(SVDQ_EINVAL, "bytes_out is NULL");
+  if (B < 1 || B > kMaxDim || M < 1 || M > kMaxDim) return set_error(SVDQ_EINVAL, "B and M must be >= 1");
+  *bytes_out = (size_t)round_up((int64_t)calib_parts(B, M) * M * 4, kAlign);
+  return SVDQ_OK;
+}
+
+int svdq_calibrate_scale(const void* x, int64_t B, int64_t M, int64_t ldx, const void* weight, int64_t N, int64_t ldw,
+                         int dtype, double alpha, float* scale_out, void* workspace, size_t workspace_bytes,
+                         svdq_stream_t stream) {
+  clear_error();
+  clear_stale_hip_error();
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (!x || !weight || !scale_out || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
+  if (B < 1 || B > kMaxDim || M < 1 || M > kMaxDim || N < 1 || N > kMaxDim)
+    return set_error(SVDQ_EINVAL, "x [B,M] and weight [M,N] must be nonempty");
+  if (ldx < M || ldw < N) return set_error(SVDQ_EINVAL, "row stride smaller than the row");
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return set_error(SVDQ_EINVAL, "alpha must be in [0, 1]");
+  size_t need = 0;
+  if ((st = svdq_calibrate_workspace_bytes(B, M, &need))) return st;
+  if (workspace_bytes < need || !aligned(workspace, kAlign)) return set_error(SVDQ_EINVAL, "workspace too small or not 256-byte aligned");
+  if (!aligned(x, dtype_size(dtype)) || !aligned(weight, dtype_size(dtype)) || !aligned(scale_out, 4))
+    return set_error(SVDQ_EINVAL, "misaligned buffer");
+  return hip_status(launch_calibrate(x, (int)B, (int)M, ldx, weight, (int)N, ldw, dtype, alpha, (float*)workspace,
+                                     scale_out, (hipStream_t)stream),
+                    "calibrate_scale launch");
+}
+
 size_t svdq_fake_quantize_workspace(int64_t rows, int64_t cols) {
   (void)cols;
   const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(rows, 1024));

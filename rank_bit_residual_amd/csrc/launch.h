@@ -89,6 +89,11 @@ inline hipError_t launch_gemm_kernel(K kernel, dim3 grid, dim3 block, unsigned s
 }
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStream_t stream);
+// Smoothing-scale calibration: per-column maxima of |x| into part[calib_parts(B, M)][M], then
+// scale[m] from them and the row maxima of |W|.
+int calib_parts(int64_t B, int64_t M);
+hipError_t launch_calibrate(const void* x, int B, int M, int64_t ldx, const void* w, int N, int64_t ldw, int dtype,
+                            double alpha, float* part, float* scale, hipStream_t stream);
 // Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
 // Per-tensor INT, bits <= 4: 64x64 tiles, K split over the waves of a block (kstages = Kp/256).

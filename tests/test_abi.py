@@ -47,6 +47,10 @@ def test_host_calls_report_errors_without_a_gpu():
     ws = ctypes.c_size_t()
     assert lib.svdq_workspace_bytes(16, 64, 48, 8, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_F32, ctypes.byref(ws)) == 0
     assert ws.value > 0
+    assert lib.svdq_calibrate_workspace_bytes(0, 64, ctypes.byref(ws)) == _lib.SVDQ_EINVAL
+    assert lib.svdq_calibrate_workspace_bytes(4096, 3072, ctypes.byref(ws)) == 0 and ws.value % 256 == 0
+    assert lib.svdq_calibrate_scale(None, 4, 4, 4, None, 4, 4, _lib.SVDQ_F32, 0.5, None, None, 0, None) == _lib.SVDQ_EINVAL
+    assert lib.svdq_calibrate_scale(None, 4, 4, 4, None, 4, 4, _lib.SVDQ_F64, 0.5, None, None, 0, None) == _lib.SVDQ_EDTYPE
     # profiling session: argument errors are reported before any HIP call
     assert lib.svdq_profile_begin(0, 8) == _lib.SVDQ_EINVAL
     assert lib.svdq_profile_begin(4, 0) == _lib.SVDQ_EINVAL

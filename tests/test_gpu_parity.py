@@ -351,3 +351,43 @@ def test_int4_gemm_shapes(B, M, N, rank, dtype):
 ])
 def test_mx_decode_batch_shapes(B, M, N, rank):
     assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- scale calibration
+def _ulp32(a):
+    a = np.abs(np.asarray(a, np.float32))
+    return np.spacing(a)
+
+
+@pytest.mark.parametrize("cid,alpha", [(1, 0.5), (2, 0.5), (3, 0.25), (5, 0.25), (4, 0.9)])
+def test_calibrate_scale_matches_oracle(cid, alpha):
+    """Exact maxima; the power and quotient in binary64 on both sides, so the float32 scales
+    agree bit for bit unless the two binary64 results straddle a float32 rounding boundary
+    (then by one ulp)."""
+    wl = WORKLOADS[cid]
+    x, w, _ = make_inputs(cid)
+    got = _np(R.calibrate_scale(_g(x, wl.dtype), _g(w, wl.dtype), alpha))
+    want = O.calibrate_scale(x, w, alpha)
+    diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert np.all(diff <= _ulp32(want)), "more than one float32 ulp apart"
+    assert np.mean(got == want) >= 0.999
+
+
+def test_calibrate_scale_edges():
+    """Zero columns and rows give 1; strided x; ragged M (not a multiple of 64) and N."""
+    rng = np.random.default_rng(22)
+    B, M, N = 37, 131, 45
+    x = O.to_dtype(rng.standard_t(3, (B, M)) * 10.0 ** rng.integers(-2, 3, (B, M)), "bf16")
+    w = O.to_dtype(rng.standard_normal((M, N)), "bf16")
+    x[:, 7] = 0.0
+    w[100] = 0.0
+    for alpha in (0.0, 0.5, 1.0):
+        xt = _g(x.T.copy(), "bf16").t()  # column-major x: the binding copies it
+        got = _np(R.calibrate_scale(xt, _g(w, "bf16"), alpha))
+        want = O.calibrate_scale(x, w, alpha)
+        assert got[7] == 1.0 and got[100] == 1.0
+        assert np.all(np.abs(got.astype(np.float64) - want) <= _ulp32(want))
+    big = torch.zeros(B, M + 9, dtype=torch.float32, device=dev())
+    big[:, 3:3 + M] = _g(x, "f32")
+    got = _np(R.calibrate_scale(big[:, 3:3 + M], _g(w, "f32"), 0.5))  # row stride M + 9, unaligned rows
+    assert np.all(np.abs(got.astype(np.float64) - O.calibrate_scale(x, w, 0.5)) <= _ulp32(O.calibrate_scale(x, w, 0.5)))
