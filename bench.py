@@ -349,6 +349,48 @@ def run_calibrate(args):
     print(json.dumps(res), flush=True)
 
 
+def toy_experiment(dev_name="cuda:0"):
+    """The exercise page's toy experiment ("SVDQuant Smoothing, Low-rank and Residual
+    Quantization", "Toy experiment") through the library on the GPU, with the oracle's numbers
+    beside it: relative output errors of naive W4A4, smoothing only, and the two-branch
+    operator at ranks 0-6, and the leading singular values of W before and after smoothing
+    (from the library's split: the column norms of L1 = U S, since L2 = V^T has orthonormal
+    rows). Inputs: the toy workload (x [16, 64] with outlier channels, W [64, 48] with a
+    rank-4 spike), float32."""
+    import numpy as np
+    import torch
+
+    import rank_bit_residual_amd as R
+    from oracle import svdquant as O
+    from workloads import make_inputs
+
+    dev = torch.device(dev_name)
+    x, w, s = make_inputs(1)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    xg, wg, sg = (torch.from_numpy(a).to(dev) for a in (x, w, s))
+
+    def err(y):
+        return O.rel_fro(y, ref)
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    lib = {"naive_w4a4": err(f64(R.fake_quantize(xg, 4)) @ f64(R.fake_quantize(wg, 4)))}
+    xs, ws = R.smooth_inputs(xg, wg, sg)
+    lib["smoothing_only"] = err(f64(R.fake_quantize(xs, 4)) @ f64(R.fake_quantize(ws, 4)))
+    lib["two_branch"] = [err(f64(R.svdquant_linear(xg, wg, sg, r, 4))) for r in range(7)]
+    orc = {"naive_w4a4": err(O.fake_quantize(x, 4, "f32").astype(np.float64) @ O.fake_quantize(w, 4, "f32"))}
+    oxs, ows = O.smooth_inputs(x, w, s, "f32")
+    orc["smoothing_only"] = err(O.fake_quantize(oxs, 4, "f32").astype(np.float64) @ O.fake_quantize(ows, 4, "f32"))
+    orc["two_branch"] = [err(O.svdquant_linear(x, w, s, r, 4)) for r in range(7)]
+    k = min(w.shape)
+    sv_lib = {name: np.linalg.norm(f64(R.split_weight(m, k)[0]), axis=0).tolist()
+              for name, m in (("W", wg.cpu()), ("smoothed_W", ws.cpu()))}
+    sv_orc = {"W": np.linalg.svd(w.astype(np.float64), compute_uv=False).tolist(),
+              "smoothed_W": np.linalg.svd(ows.astype(np.float64), compute_uv=False).tolist()}
+    return {"library": lib, "oracle": orc, "singular_values_library": sv_lib, "singular_values_oracle": sv_orc}
+
+
 def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, wl, command):
     """Per-dispatch HBM bytes of the residual GEMM from rocprofv3 counter CSVs (FETCH_SIZE and
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain
@@ -392,6 +434,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_BYTES"))
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--toy-experiment", action="store_true",
+                    help="run the exercise page's toy experiment through the library and print its error table")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the smoothing-scale calibration on the workload's x and W instead of the operator")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
@@ -419,7 +463,9 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    if args.calibrate:
+    if args.toy_experiment:
+        print(json.dumps(toy_experiment()), flush=True)
+    elif args.calibrate:
         run_calibrate(args)
     else:
         run(args)

@@ -391,3 +391,26 @@ def test_calibrate_scale_edges():
     big[:, 3:3 + M] = _g(x, "f32")
     got = _np(R.calibrate_scale(big[:, 3:3 + M], _g(w, "f32"), 0.5))  # row stride M + 9, unaligned rows
     assert np.all(np.abs(got.astype(np.float64) - O.calibrate_scale(x, w, 0.5)) <= _ulp32(O.calibrate_scale(x, w, 0.5)))
+
+
+# ----------------------------------------------------------------------------- toy experiment
+def test_toy_experiment_through_library():
+    """The exercise page's toy experiment run through the library: the same ordering as the
+    page describes (two-branch below smoothing-only below naive W4A4, falling with rank), the
+    oracle's numbers for naive and smoothing-only (bit-exact quantisation), the two-branch
+    errors within 2% of the oracle's (different but equivalent truncated-SVD bases), and the
+    singular values from the library's split equal to numpy's."""
+    dev()
+    import bench
+
+    r = bench.toy_experiment()
+    lib, orc = r["library"], r["oracle"]
+    assert lib["naive_w4a4"] == pytest.approx(orc["naive_w4a4"], rel=1e-12)
+    assert lib["smoothing_only"] == pytest.approx(orc["smoothing_only"], rel=1e-12)
+    assert np.allclose(lib["two_branch"], orc["two_branch"], rtol=0.02)
+    tb = lib["two_branch"]
+    assert tb[6] < tb[0] and tb[4] < lib["smoothing_only"] < lib["naive_w4a4"]
+    for name in ("W", "smoothed_W"):
+        a = np.array(r["singular_values_library"][name])
+        b = np.array(r["singular_values_oracle"][name])
+        assert np.allclose(a[:8], b[:8], rtol=1e-5, atol=1e-6 * b[0])
