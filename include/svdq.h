@@ -178,6 +178,13 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
 int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
                  int64_t rank, int fmt, int bits, int dtype, void* blob_host,
                  void* left_out, void* right_out, void* residual_out);
+/* The same preparation from a weight in the Linear layout ([FI] Parameters: the weight as
+ * [n, k], output channels by input channels): weight_nm is [N, M] with host row stride
+ * ldw >= M and holds W transposed. The blob (and the optional factor outputs, still in the
+ * [M, N] orientation) are byte for byte those of svdq_prepare on W. Errors as svdq_prepare. */
+int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw, const float* scale,
+                        int64_t rank, int fmt, int bits, int dtype, void* blob_host,
+                        void* left_out, void* right_out, void* residual_out);
 
 /* --------------------------------------------------------------------------------------
  * Workspace of svdq_linear / svdq_quantize_activations: device scratch the caller

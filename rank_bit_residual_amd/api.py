@@ -194,17 +194,23 @@ def prepared_layout(M: int, N: int, rank: int, fmt: str = "int", bits: int = 4, 
 
 
 def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4, fmt: str = "int",
-            device=None, keep_factors: bool = False) -> Prepared:
+            device=None, keep_factors: bool = False, layout: str = "mn") -> Prepared:
     """One-time preparation: fold scale into W, split, quantise and pack the residual (host),
-    then copy the blob to ``device`` (default: the weight's device, which must be a GPU)."""
+    then copy the blob to ``device`` (default: the weight's device, which must be a GPU).
+
+    ``layout="mn"`` takes W as [M, N] (input by output channels); ``layout="nm"`` takes a
+    Linear-layout weight [N, M] (output by input channels, i.e. W transposed) without a copy
+    into the other orientation; both give the same blob."""
+    if layout not in ("mn", "nm"):
+        raise ValueError('layout must be "mn" ([M, N]) or "nm" (Linear layout [N, M])')
     if weight.dim() != 2 or scale.dim() != 1:
         raise ValueError("weight must be 2-D and scale 1-D")
-    if scale.shape[0] != weight.shape[0]:
-        raise ValueError("scale must have one entry per input channel (weight.shape[0])")
+    M, N = weight.shape if layout == "mn" else (weight.shape[1], weight.shape[0])
+    if scale.shape[0] != M:
+        raise ValueError("scale must have one entry per input channel")
     _check_rank(weight, rank)
     _check_int("bits", bits)
     lib = L.load()
-    M, N = weight.shape
     code = _dtype_code(weight)
     offs = prepared_layout(M, N, rank, fmt, bits, weight.dtype)  # raises for float64
     host_w = weight.detach().to("cpu").contiguous()
@@ -215,9 +221,11 @@ def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4,
         left = torch.empty((M, rank), dtype=weight.dtype)
         right = torch.empty((rank, N), dtype=weight.dtype)
         res = torch.empty((M, N), dtype=weight.dtype)
-    L.check(lib.svdq_prepare(_ptr(host_w), M, N, N, _ptr(host_s), rank, _fmt_code(fmt), bits, code, _ptr(blob),
-                             _ptr(left) if keep_factors and rank else None,
-                             _ptr(right) if keep_factors and rank else None, _ptr(res)))
+    fn, ld = (lib.svdq_prepare, N) if layout == "mn" else (lib.svdq_prepare_linear, M)
+    a, b = (M, N) if layout == "mn" else (N, M)
+    L.check(fn(_ptr(host_w), a, b, ld, _ptr(host_s), rank, _fmt_code(fmt), bits, code, _ptr(blob),
+               _ptr(left) if keep_factors and rank else None, _ptr(right) if keep_factors and rank else None,
+               _ptr(res)))
     dev = weight.device if device is None else torch.device(device)
     # a host blob is only for inspection; linear() needs it on the GPU
     return Prepared(blob.to(dev), M, N, rank, fmt, bits, weight.dtype, offs, left, right, res)

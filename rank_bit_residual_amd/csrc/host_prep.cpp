@@ -95,13 +95,15 @@ inline uint16_t double_to_bf16_bits(double v) {
   return (uint16_t)(u >> 16);
 }
 
-struct HostMat {  // read-only view of a dtype matrix on the host
+struct HostMat {  // read-only view of a dtype matrix on the host: element (i, j)
   const void* p;
   int64_t ld;
   int dtype;
+  bool trans = false;  // stored transposed: (i, j) at p[j * ld + i]
   float at(int64_t i, int64_t j) const {
-    if (dtype == SVDQ_F32) return ((const float*)p)[i * ld + j];
-    return bf16_bits_to_float(((const uint16_t*)p)[i * ld + j]);
+    const int64_t k = trans ? j * ld + i : i * ld + j;
+    if (dtype == SVDQ_F32) return ((const float*)p)[k];
+    return bf16_bits_to_float(((const uint16_t*)p)[k]);
   }
 };
 
@@ -241,12 +243,35 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
   return SVDQ_OK;
 }
 
+static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
+                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out);
+
 int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale, int64_t rank, int fmt,
                  int bits, int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out) {
   clear_error();
   int st = validate_prepare(M, N, ldw, rank, fmt, bits, dtype);
   if (st) return st;
   if (!weight || !scale || !blob_host) return set_error(SVDQ_EINVAL, "NULL buffer passed to prepare");
+  return prepare_impl(HostMat{weight, ldw, dtype, false}, M, N, scale, rank, fmt, bits, dtype, blob_host, left_out,
+                      right_out, residual_out);
+}
+
+int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw, const float* scale, int64_t rank,
+                        int fmt, int bits, int dtype, void* blob_host, void* left_out, void* right_out,
+                        void* residual_out) {
+  clear_error();
+  // validate as the [M, N] matrix it is the transpose of; the row stride runs over M here
+  int st = validate_prepare(M, N, N, rank, fmt, bits, dtype);
+  if (st) return st;
+  if (ldw < M) return set_error(SVDQ_EINVAL, "weight row stride smaller than M");
+  if (!weight_nm || !scale || !blob_host) return set_error(SVDQ_EINVAL, "NULL buffer passed to prepare");
+  return prepare_impl(HostMat{weight_nm, ldw, dtype, true}, M, N, scale, rank, fmt, bits, dtype, blob_host, left_out,
+                      right_out, residual_out);
+}
+
+static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
+                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out) {
+  int st;
   if ((st = svdq_check_smoothing(1, M, M, M, N, scale))) return st;
   const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
   int64_t off[SVDQ_NSEC];
@@ -255,7 +280,6 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
   std::memset(blob, 0, (size_t)off[SVDQ_SEC_END]);
 
   // fold: ws = D(scale[m] * W[m,n]), one binary32 multiply and one rounding
-  HostMat W{weight, ldw, dtype};
   std::vector<float> ws((size_t)(M * N));
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < M; i++)

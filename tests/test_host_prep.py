@@ -214,3 +214,18 @@ def test_device_calls_need_a_gpu():
     p = _prep(w, s, "f32", 4, "int", 4)
     with pytest.raises(RuntimeError):
         R.linear(x, p)
+
+
+@pytest.mark.parametrize("name,rank,fmt,bits", [("bf16_small", 32, "mx", 4), ("toy", 8, "int", 4),
+                                                ("f32_mid", 16, "mx", 4), ("bf16_ragged", 7, "int", 6)])
+def test_linear_layout_prepare_gives_the_same_blob(name, rank, fmt, bits):
+    """A weight handed over in the Linear layout [N, M] (W transposed) prepares to the same
+    bytes, and the same factors, as W itself."""
+    w, s, dtype = _case(name)
+    a = R.prepare(_t(w, dtype), torch.from_numpy(s), rank, bits, fmt, device="cpu", keep_factors=True)
+    b = R.prepare(_t(w.T.copy(), dtype), torch.from_numpy(s), rank, bits, fmt, device="cpu", keep_factors=True,
+                  layout="nm")
+    assert torch.equal(a.blob, b.blob)
+    assert torch.equal(a.residual, b.residual) and (rank == 0 or torch.equal(a.left, b.left))
+    with pytest.raises(ValueError):
+        R.prepare(_t(w.T.copy(), dtype), torch.from_numpy(s), rank, bits, fmt, device="cpu", layout="km")
