@@ -215,6 +215,14 @@ int svdq_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt,
 int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob,
                 int64_t N, int64_t rank, int fmt, int bits, int dtype,
                 void* y, int64_t ldy, void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+/* The same with a per-output-channel bias ([FI] Parameters: optional bias of the GEMM):
+ * Y = D( Q(X^) Q(R) + down L2 + bias ), bias: device [N] of dtype (or NULL: svdq_linear),
+ * added in fp32 before the single output rounding. Errors as svdq_linear, plus EINVAL for
+ * a misaligned bias. */
+int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob,
+                     int64_t N, int64_t rank, int fmt, int bits, int dtype, const void* bias,
+                     void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                     svdq_stream_t stream);
 
 /* --------------------------------------------------------------------------------------
  * svdq_quantize_activations — step (a) alone, for bit-exact checks ([EX] "Formula and

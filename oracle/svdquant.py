@@ -251,8 +251,9 @@ def pack_int_codes(codes, bits: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- the operator
-def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str) -> np.ndarray:
-    """[P1] "Formula and conventions" item 3, Y = (X^ L1) L2 + Q(X^) Q(R), in float64.
+def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str, bias=None) -> np.ndarray:
+    """[P1] "Formula and conventions" item 3, Y = (X^ L1) L2 + Q(X^) Q(R), in float64, plus an
+    optional per-output-channel bias [N] (the GPU library page's optional bias parameter).
 
     X^ = D(x/scale). The low-rank branch uses the unquantised X^ and the stored
     factors; only R is quantised on the weight side. fmt "int": per-tensor INT
@@ -273,7 +274,10 @@ def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str
         res = dequant_mx(cx, bx) @ dequant_mx(cr, br).T
     else:
         raise ValueError(f"unknown format {fmt!r}")
-    return low + res
+    y = low + res
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
 
 
 def svdquant_linear(x, weight, scale, rank: int, bits: int = 4):

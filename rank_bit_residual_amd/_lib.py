@@ -28,6 +28,8 @@ SIGNATURES = {
     "svdq_workspace_bytes": (c_int, [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]),
     "svdq_linear": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                             c_sz, c_vp]),
+    "svdq_linear_bias": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp,
+                                 c_i64, c_vp, c_sz, c_vp]),
     "svdq_quantize_activations": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                                           c_i64, c_vp, c_vp, c_sz, c_vp]),
     "svdq_prepare_linear": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),

@@ -239,8 +239,8 @@ def workspace_bytes(B: int, prep: Prepared) -> int:
 
 
 def linear(x: torch.Tensor, prep: Prepared, out: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """The per-call operator Y = (X^ L1) L2 + Q(X^) Q(R) on prepared weights."""
+           workspace: torch.Tensor | None = None, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """The per-call operator Y = (X^ L1) L2 + Q(X^) Q(R) (+ bias[N]) on prepared weights."""
     _require_gpu(x, prep.blob)
     if prep.blob.device != x.device:
         raise ValueError("x and the prepared weights must be on the same device")
@@ -256,9 +256,14 @@ def linear(x: torch.Tensor, prep: Prepared, out: torch.Tensor | None = None,
     wsb = workspace_bytes(B, prep)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
-    L.check(L.load().svdq_linear(_ptr(x), B, prep.M, x.stride(0), _ptr(prep.blob), prep.N, prep.rank,
-                                 _fmt_code(prep.fmt), prep.bits, _DT[prep.dtype], _ptr(out), out.stride(0),
-                                 _ptr(workspace), workspace.numel(), _stream(x)))
+    if bias is not None:
+        if bias.dim() != 1 or bias.shape[0] != prep.N or bias.dtype != x.dtype or bias.device != x.device:
+            raise ValueError(f"bias must be a [{prep.N}] tensor with x's dtype and device")
+        bias = bias.contiguous()
+    L.check(L.load().svdq_linear_bias(_ptr(x), B, prep.M, x.stride(0), _ptr(prep.blob), prep.N, prep.rank,
+                                      _fmt_code(prep.fmt), prep.bits, _DT[prep.dtype],
+                                      _ptr(bias) if bias is not None else None, _ptr(out), out.stride(0),
+                                      _ptr(workspace), workspace.numel(), _stream(x)))
     return out
 
 

@@ -270,10 +270,18 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
 int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob, int64_t N, int64_t rank, int fmt,
                 int bits, int dtype, void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                 svdq_stream_t stream) {
+  return svdq_linear_bias(x, B, M, ldx, blob, N, rank, fmt, bits, dtype, nullptr, y, ldy, workspace, workspace_bytes,
+                          stream);
+}
+
+int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob, int64_t N, int64_t rank,
+                     int fmt, int bits, int dtype, const void* bias, void* y, int64_t ldy, void* workspace,
+                     size_t workspace_bytes, svdq_stream_t stream) {
   clear_error();
   clear_stale_hip_error();
   int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
   if (st) return st;
+  if (bias && !aligned(bias, dtype_size(dtype))) return set_error(SVDQ_EINVAL, "bias misaligned");
   if (!x || !blob || !y || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
   if (ldx < M) return set_error(SVDQ_EINVAL, "x row stride smaller than M");
   if (ldy < N) return set_error(SVDQ_EINVAL, "y row stride smaller than N");
@@ -350,6 +358,7 @@ int svdq_linear(const void* x, int64_t B, int64_t M, int64_t ldx, const void* bl
   g.l2t = bl + boff[SVDQ_SEC_L2T];
   g.rp = (int)d.rp;
   g.y = y;
+  g.bias = bias;
   g.ldy = ldy;
   g.B = (int)B;
   g.N = (int)N;

@@ -231,6 +231,14 @@ __device__ inline float down1_f32(const void* down, const float* part, int chunk
   return s;
 }
 
+// ---- output bias ----------------------------------------------------------------------
+// bias[min(col, N - 1)] as f32, or 0 without a bias (columns past N are never stored).
+template <class DT>
+__device__ inline float bias_at(const void* bias, int col, int N) {
+  if (!bias) return 0.f;
+  return DT::to_f32(reinterpret_cast<const typename DT::T*>(bias)[col < N ? col : N - 1]);
+}
+
 // ---- wave / block reductions ------------------------------------------------------------
 __device__ inline float wave_max(float v) {
 #pragma unroll

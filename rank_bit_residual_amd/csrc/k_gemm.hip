@@ -244,6 +244,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int nt = 0; nt < 2; nt++) {
       const int col = n0 + bcol[nt];
+      const float bz = bias_at<DT>(p.bias, col, p.N);
+#pragma unroll
+      for (int v = 0; v < 16; v++) f[mt][nt][v] += bz;
       if (col >= p.N) continue;
 #pragma unroll
       for (int v = 0; v < 16; v++) {

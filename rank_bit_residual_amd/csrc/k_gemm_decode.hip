@@ -222,11 +222,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
       const int col = n0 + 16 * tt + i;
+      const float bz = bias_at<BF16>(p.bias, col, p.N);
       if (col >= p.N) continue;
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int row = 16 * m + 4 * g + v;
-        if (row < p.B) y[(int64_t)row * p.ldy + col] = BF16::from_f32(acc[m][tt][v]);
+        if (row < p.B) y[(int64_t)row * p.ldy + col] = BF16::from_f32(acc[m][tt][v] + bz);
       }
     }
 }

@@ -290,7 +290,12 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
     }
   }
 
-  // ---- round once, stage the 64 x 64 tile in LDS and write it with 16-byte stores
+  // ---- bias, round once, stage the 64 x 64 tile in LDS and write it with 16-byte stores
+  {
+    const float bz = bias_at<DT>(p.bias, col, p.N);
+#pragma unroll
+    for (int v = 0; v < 16; v++) f[v] += bz;
+  }
   __syncthreads();  // every wave has read its partial sums
   T* tile = reinterpret_cast<T*>(smem);
 #pragma unroll

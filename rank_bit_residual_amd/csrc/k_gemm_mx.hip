@@ -304,6 +304,18 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   stage(nst - 2, fa, sa, fb, sb, LastButOne());
   stage(nst - 1, fb, sb, fa, sa, Last());
 
+  // ---- output bias (one column per lane and 32x32 tile)
+  if (p.bias) {
+#pragma unroll
+    for (int j = 0; j < C::NT; j++) {
+      const float bz = bias_at<DT>(p.bias, n0 + wn * C::TN + 32 * j + l32, p.N);
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[i][j][v] += bz;
+    }
+  }
+
   // ---- epilogue: one rounding, staged through the (now idle) LDS ring for 16-byte stores. In a
   // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Neighbouring lanes
   // swap one value (DPP quad_perm [1,0,3,2]) so that the even lane holds row 8q + 4g + e,

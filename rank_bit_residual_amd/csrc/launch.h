@@ -49,6 +49,7 @@ struct GemmParams {
   int rp;
   void* y;
   int64_t ldy;
+  const void* bias;  // [N] dtype added before the output rounding, or nullptr
   int B, N, kstages;
   int npad;  // rows of the prepared weight (N rounded up); loads clamp to npad - 1
 };

@@ -414,3 +414,43 @@ def test_toy_experiment_through_library():
         a = np.array(r["singular_values_library"][name])
         b = np.array(r["singular_values_oracle"][name])
         assert np.allclose(a[:8], b[:8], rtol=1e-5, atol=1e-6 * b[0])
+
+
+# ----------------------------------------------------------------------------- output bias
+@pytest.mark.parametrize("B,M,N,fmt,dtype", [
+    (40, 2048, 300, "int", "bf16"),   # INT4 kernel
+    (512, 512, 576, "mx", "bf16"),    # large-batch MXFP4 kernel (256 x 192 tiles)
+    (16, 1024, 200, "mx", "bf16"),    # decode MXFP4 kernel
+    (48, 320, 130, "int", "f32"),     # generic kernel
+])
+def test_linear_bias_matches_oracle(B, M, N, fmt, dtype):
+    rng = np.random.default_rng(B + N)
+    x = O.to_dtype(rng.standard_t(3, (B, M)), dtype)
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 2)) @ rng.standard_normal((2, N)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.5)
+    bias = O.to_dtype(rng.standard_normal(N), dtype)
+    p = R.prepare(_g(w, dtype), torch.from_numpy(s), 32, 4, fmt, keep_factors=True)
+    xg = _g(x, dtype)
+    y = R.linear(xg, p, bias=_g(bias, dtype))
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), fmt, 4, dtype, bias=bias)
+    assert O.rel_fro(_np(y), ref) <= TOL[dtype]
+    # without the bias the result is the plain operator
+    y0 = R.linear(xg, p)
+    ref0 = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), fmt, 4, dtype)
+    assert O.rel_fro(_np(y0), ref0) <= TOL[dtype]
+
+
+def test_linear_bias_exact_special_case():
+    """Rank 0, unit scale, integer x and W with max 7 (exact INT4 product) plus an integer
+    bias: Y = x @ W + bias bit for bit."""
+    rng = np.random.default_rng(23)
+    B, M, N = 40, 320, 300
+    x = rng.integers(-7, 8, (B, M)).astype(np.float32)
+    w = rng.integers(-7, 8, (M, N)).astype(np.float32)
+    x[0, 0] = w[0, 0] = 7
+    bias = rng.integers(-50, 50, N).astype(np.float32)
+    p = R.prepare(_g(w, "f32"), torch.ones(M), 0, 4, "int")
+    y = R.linear(_g(x, "f32"), p, bias=_g(bias, "f32"))
+    want = x.astype(np.float64) @ w.astype(np.float64) + bias
+    assert np.array_equal(_bits(_np(y)), _bits(want.astype(np.float32)))

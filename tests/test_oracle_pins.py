@@ -425,3 +425,16 @@ def test_calibrate_scale_rejects(alpha):
         O.calibrate_scale(np.ones((2, 3), np.float32), np.ones((3, 2), np.float32), alpha)
     with pytest.raises(ValueError):
         O.calibrate_scale(np.ones((2, 3), np.float32), np.ones((4, 2), np.float32), 0.5)
+
+
+def test_forward_bias_is_added_per_output_channel():
+    """Zero activations give codes 0 and a zero low-rank branch, so Y is the bias itself; a
+    bias shifts every row of a nonzero forward by the same vector."""
+    x, w, s = make_inputs(1)
+    left, right, res = O.split_weight(O.smooth_weight(w, s, "f32"), 8, "f32")
+    bias = np.arange(w.shape[1], dtype=np.float32) - 20.0
+    y0 = O.forward_ref(np.zeros_like(x), s, left, right, res, "int", 4, "f32", bias=bias)
+    assert np.array_equal(y0, np.broadcast_to(bias.astype(np.float64), y0.shape))
+    y = O.forward_ref(x, s, left, right, res, "mx", 4, "f32")
+    yb = O.forward_ref(x, s, left, right, res, "mx", 4, "f32", bias=bias)
+    assert np.allclose(yb - y, bias[None, :], rtol=0, atol=1e-12 * np.abs(y).max())
