@@ -349,6 +349,34 @@ def run_calibrate(args):
     print(json.dumps(res), flush=True)
 
 
+def run_prepare(args):
+    """One-time preparation of the workload's weight (fold, truncated SVD, residual
+    quantisation and packing): the host route and the route with the SVD's large products on
+    the GPU, timed once each (wall clock, including the blob copy to the device)."""
+    import numpy as np
+    import torch
+
+    import rank_bit_residual_amd as R
+    from workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x, w, s = make_inputs(wl, B=min(wl.B, 64))
+    wt = torch.from_numpy(w).to(td)
+    out = {"metric": "one-time preparation seconds (fold + truncated SVD + residual quantisation)",
+           "unit": "s", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+           "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "rank": wl.rank, "format": wl.fmt}}
+    for name, gpu in (("host", False), ("gpu_svd", True)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p = R.prepare(wt, torch.from_numpy(s), wl.rank, wl.bits, wl.fmt, device=dev, keep_factors=True, svd_on_gpu=gpu)
+        torch.cuda.synchronize()
+        out[name + "_s"] = time.perf_counter() - t0
+        out[name + "_residual_fro"] = float(np.linalg.norm(p.residual.to(torch.float32).numpy()))
+    print(json.dumps(out), flush=True)
+
+
 def toy_experiment(dev_name="cuda:0"):
     """The exercise page's toy experiment ("SVDQuant Smoothing, Low-rank and Residual
     Quantization", "Toy experiment") through the library on the GPU, with the oracle's numbers
@@ -436,6 +464,8 @@ def main():
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--toy-experiment", action="store_true",
                     help="run the exercise page's toy experiment through the library and print its error table")
+    ap.add_argument("--prepare", action="store_true",
+                    help="time the one-time weight preparation on the host and with the GPU SVD products")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the smoothing-scale calibration on the workload's x and W instead of the operator")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
@@ -463,7 +493,9 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    if args.toy_experiment:
+    if args.prepare:
+        run_prepare(args)
+    elif args.toy_experiment:
         print(json.dumps(toy_experiment()), flush=True)
     elif args.calibrate:
         run_calibrate(args)

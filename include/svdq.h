@@ -178,6 +178,20 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
 int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
                  int64_t rank, int fmt, int bits, int dtype, void* blob_host,
                  void* left_out, void* right_out, void* residual_out);
+/* The same preparation with the truncated SVD's large products (the randomized subspace
+ * iteration's panel products with the smoothed weight, in float64) on the GPU; the small
+ * dense steps, the fold, the residual and the quantisation stay on the host, so the result
+ * satisfies the same contract (a best rank-r approximation up to the randomized route's
+ * accuracy). Matrices with min(M, N) <= 512 take the host's full Jacobi route and need no
+ * workspace. workspace: device, 256-byte aligned, >= svdq_prepare_gpu_workspace_bytes
+ * bytes; the call enqueues copies and kernels on `stream` and waits for them (host call).
+ * Errors as svdq_prepare, plus EINVAL for a small workspace and EHIP. */
+int svdq_prepare_gpu_workspace_bytes(int64_t M, int64_t N, int64_t rank, size_t* bytes_out);
+int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
+                     int64_t rank, int fmt, int bits, int dtype, void* blob_host,
+                     void* left_out, void* right_out, void* residual_out,
+                     void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+
 /* The same preparation from a weight in the Linear layout ([FI] Parameters: the weight as
  * [n, k], output channels by input channels): weight_nm is [N, M] with host row stride
  * ldw >= M and holds W transposed. The blob (and the optional factor outputs, still in the

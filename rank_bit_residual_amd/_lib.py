@@ -32,6 +32,9 @@ SIGNATURES = {
                                  c_i64, c_vp, c_sz, c_vp]),
     "svdq_quantize_activations": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                                           c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "svdq_prepare_gpu_workspace_bytes": (c_int, [c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]),
+    "svdq_prepare_gpu": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
+                                 c_vp, c_sz, c_vp]),
     "svdq_prepare_linear": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "svdq_calibrate_workspace_bytes": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "svdq_calibrate_scale": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, ctypes.c_double, c_vp, c_vp,

@@ -194,13 +194,14 @@ def prepared_layout(M: int, N: int, rank: int, fmt: str = "int", bits: int = 4, 
 
 
 def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4, fmt: str = "int",
-            device=None, keep_factors: bool = False, layout: str = "mn") -> Prepared:
+            device=None, keep_factors: bool = False, layout: str = "mn", svd_on_gpu: bool = False) -> Prepared:
     """One-time preparation: fold scale into W, split, quantise and pack the residual (host),
     then copy the blob to ``device`` (default: the weight's device, which must be a GPU).
 
     ``layout="mn"`` takes W as [M, N] (input by output channels); ``layout="nm"`` takes a
     Linear-layout weight [N, M] (output by input channels, i.e. W transposed) without a copy
-    into the other orientation; both give the same blob."""
+    into the other orientation; both give the same blob. ``svd_on_gpu`` runs the truncated
+    SVD's large products on ``device`` (layout "mn" only)."""
     if layout not in ("mn", "nm"):
         raise ValueError('layout must be "mn" ([M, N]) or "nm" (Linear layout [N, M])')
     if weight.dim() != 2 or scale.dim() != 1:
@@ -221,12 +222,22 @@ def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4,
         left = torch.empty((M, rank), dtype=weight.dtype)
         right = torch.empty((rank, N), dtype=weight.dtype)
         res = torch.empty((M, N), dtype=weight.dtype)
-    fn, ld = (lib.svdq_prepare, N) if layout == "mn" else (lib.svdq_prepare_linear, M)
-    a, b = (M, N) if layout == "mn" else (N, M)
-    L.check(fn(_ptr(host_w), a, b, ld, _ptr(host_s), rank, _fmt_code(fmt), bits, code, _ptr(blob),
-               _ptr(left) if keep_factors and rank else None, _ptr(right) if keep_factors and rank else None,
-               _ptr(res)))
     dev = weight.device if device is None else torch.device(device)
+    outs = (_ptr(left) if keep_factors and rank else None, _ptr(right) if keep_factors and rank else None, _ptr(res))
+    if svd_on_gpu:
+        if layout != "mn" or dev.type != "cuda":
+            raise ValueError("svd_on_gpu needs layout 'mn' and a GPU device")
+        need = ctypes.c_size_t()
+        L.check(lib.svdq_prepare_gpu_workspace_bytes(M, N, rank, ctypes.byref(need)))
+        work = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        L.check(lib.svdq_prepare_gpu(_ptr(host_w), M, N, N, _ptr(host_s), rank, _fmt_code(fmt), bits, code,
+                                     _ptr(blob), *outs, _ptr(work), need.value, ctypes.c_void_p(stream.cuda_stream)))
+        del work
+    else:
+        fn, ld = (lib.svdq_prepare, N) if layout == "mn" else (lib.svdq_prepare_linear, M)
+        a, b = (M, N) if layout == "mn" else (N, M)
+        L.check(fn(_ptr(host_w), a, b, ld, _ptr(host_s), rank, _fmt_code(fmt), bits, code, _ptr(blob), *outs))
     # a host blob is only for inspection; linear() needs it on the GPU
     return Prepared(blob.to(dev), M, N, rank, fmt, bits, weight.dtype, offs, left, right, res)
 

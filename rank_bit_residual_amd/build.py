@@ -29,6 +29,7 @@ HIP_SOURCES = {
     "k_gemm_decode.hip": [],
     "k_gemm_int.hip": [],
     "k_calib.hip": [],
+    "k_svd.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

@@ -165,8 +165,15 @@ int validate_prepare(int64_t M, int64_t N, int64_t ldw, int64_t rank, int fmt, i
 }
 
 // Split ws [M,N] (float values exact in dtype) into rounded factors and the residual.
+// Where the truncated SVD runs: the host, or the GPU for the randomized route's products.
+struct SplitDevice {
+  void* workspace = nullptr;
+  void* stream = nullptr;
+  int hip_error = 0;
+};
+
 void split(const std::vector<float>& ws, int64_t M, int64_t N, int64_t rank, int dtype, std::vector<float>& L1,
-           std::vector<float>& L2, std::vector<float>& R) {
+           std::vector<float>& L2, std::vector<float>& R, SplitDevice* dev = nullptr) {
   L1.assign((size_t)(M * rank), 0.f);
   L2.assign((size_t)(rank * N), 0.f);
   R.assign((size_t)(M * N), 0.f);
@@ -175,7 +182,10 @@ void split(const std::vector<float>& ws, int64_t M, int64_t N, int64_t rank, int
     return;
   }
   std::vector<double> l1((size_t)(M * rank)), l2((size_t)(rank * N));
-  host::truncated_svd(ws.data(), M, N, N, rank, l1.data(), l2.data());
+  if (dev)
+    dev->hip_error = run_split_on_device(ws.data(), M, N, rank, dev->workspace, dev->stream, l1.data(), l2.data());
+  else
+    host::truncated_svd(ws.data(), M, N, N, rank, l1.data(), l2.data());
   for (size_t i = 0; i < l1.size(); i++) L1[i] = round_f64(l1[i], dtype);
   for (size_t i = 0; i < l2.size(); i++) L2[i] = round_f64(l2[i], dtype);
   // R = D(ws - L1 L2), the product in float64 from the stored factors
@@ -244,7 +254,36 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
 }
 
 static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
-                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out);
+                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out,
+                        SplitDevice* dev = nullptr);
+
+int svdq_prepare_gpu_workspace_bytes(int64_t M, int64_t N, int64_t rank, size_t* bytes_out) {
+  clear_error();
+  if (!bytes_out) return set_error(SVDQ_EINVAL, "bytes_out is NULL");
+  if (M < 1 || N < 1 || rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "bad shape or rank");
+  const int64_t k = host::randomized_panel_columns(M, N, rank);
+  *bytes_out = k ? device_panels_bytes(M, N, k) : 0;
+  return SVDQ_OK;
+}
+
+int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale, int64_t rank, int fmt,
+                     int bits, int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out,
+                     void* workspace, size_t workspace_bytes, svdq_stream_t stream) {
+  clear_error();
+  int st = validate_prepare(M, N, ldw, rank, fmt, bits, dtype);
+  if (st) return st;
+  if (!weight || !scale || !blob_host) return set_error(SVDQ_EINVAL, "NULL buffer passed to prepare");
+  size_t need = 0;
+  if ((st = svdq_prepare_gpu_workspace_bytes(M, N, rank, &need))) return st;
+  if (need && (!workspace || workspace_bytes < need || (uintptr_t)workspace % kAlign))
+    return set_error(SVDQ_EINVAL, "device workspace too small or not 256-byte aligned");
+  SplitDevice dev{workspace, (void*)stream, 0};
+  st = prepare_impl(HostMat{weight, ldw, dtype, false}, M, N, scale, rank, fmt, bits, dtype, blob_host, left_out,
+                    right_out, residual_out, &dev);
+  if (st) return st;
+  if (dev.hip_error) return set_error(SVDQ_EHIP, "device products of the truncated SVD failed");
+  return SVDQ_OK;
+}
 
 int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale, int64_t rank, int fmt,
                  int bits, int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out) {
@@ -270,7 +309,8 @@ int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw
 }
 
 static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
-                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out) {
+                        int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out,
+                        SplitDevice* dev) {
   int st;
   if ((st = svdq_check_smoothing(1, M, M, M, N, scale))) return st;
   const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
@@ -286,7 +326,7 @@ static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* sca
     for (int64_t j = 0; j < N; j++) ws[i * N + j] = round_f32(scale[i] * W.at(i, j), dtype);
 
   std::vector<float> L1, L2, R;
-  split(ws, M, N, rank, dtype, L1, L2, R);
+  split(ws, M, N, rank, dtype, L1, L2, R, dev);
 
   std::memcpy(blob + off[SVDQ_SEC_SCALE], scale, (size_t)M * 4);
   {

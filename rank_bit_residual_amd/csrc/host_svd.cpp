@@ -310,24 +310,31 @@ void full_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, doub
 }
 
 void randomized_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, int64_t k, int power_iters,
-                    double* L1, double* L2) {
+                    double* L1, double* L2, PanelProducts* dev) {
+  // the large products with A: on the host, or through the backend
+  auto prod = [&](int kind, const double* P, double* C) {
+    if (dev)
+      dev->product(kind, k, P, C);
+    else if (kind == 0)
+      gemm<double, float>(k, N, M, P, M, 1, A, lda, 1, C, N);  // C^T [k x N] = P^T [k x M] * A [M x N]
+    else
+      gemm<double, float>(k, M, N, P, N, 1, A, 1, lda, C, M);  // C^T [k x M] = P^T [k x N] * A^T [N x M]
+  };
   // Panels are stored column-major: column c of a [rows x k] panel at P + c*rows.
   std::vector<double> Om((size_t)N * k), Q((size_t)M * k), Z((size_t)N * k);
   Normal rng(0x5EEDull + (uint64_t)M * 1000003ull + (uint64_t)N);
   for (auto& v : Om) v = rng();
-  // Y = A * Om: Y^T [k x M] = Om^T [k x N] * A^T [N x M]
-  gemm<double, float>(k, M, N, Om.data(), N, 1, A, 1, lda, Q.data(), M);
+  prod(1, Om.data(), Q.data());  // Y = A * Om
   orthonormalize(Q.data(), M, k, 11);
   for (int it = 0; it < power_iters; it++) {
-    // Z = A^T Q: Z^T [k x N] = Q^T [k x M] * A [M x N]
-    gemm<double, float>(k, N, M, Q.data(), M, 1, A, lda, 1, Z.data(), N);
+    prod(0, Q.data(), Z.data());  // Z = A^T Q
     orthonormalize(Z.data(), N, k, 101 + it);
-    gemm<double, float>(k, M, N, Z.data(), N, 1, A, 1, lda, Q.data(), M);
+    prod(1, Z.data(), Q.data());  // Q = A Z
     orthonormalize(Q.data(), M, k, 1001 + it);
   }
   // Rayleigh-Ritz: Bs = Q^T A [k x N] (row l = column l of Bs^T), Bs^T J = W.
   std::vector<double> Bs((size_t)k * N), J((size_t)k * k);
-  gemm<double, float>(k, N, M, Q.data(), M, 1, A, lda, 1, Bs.data(), N);
+  prod(0, Q.data(), Bs.data());
   jacobi_columns(Bs.data(), N, k, N, J.data(), k);
   std::vector<double> sigma;
   auto ord = order_by_norm(Bs.data(), N, k, N, sigma);
@@ -346,17 +353,20 @@ void randomized_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r
 
 }  // namespace
 
-void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2) {
-  if (r <= 0) return;
+int64_t randomized_panel_columns(int64_t M, int64_t N, int64_t r) {
   const int64_t n = std::min(M, N);
   const int64_t k = std::min(n, r + 32);
-  if (n <= 512 || k >= n) {
+  return (r <= 0 || n <= 512 || k >= n) ? 0 : k;
+}
+
+void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2,
+                   PanelProducts* dev) {
+  if (r <= 0) return;
+  const int64_t k = randomized_panel_columns(M, N, r);
+  if (k == 0)
     full_svd(A, M, N, lda, r, L1, L2);
-  } else {
-    const char* env = std::getenv("SVDQ_POWER_ITERS");
-    const int q = env ? std::max(0, std::atoi(env)) : 16;
-    randomized_svd(A, M, N, lda, r, k, q, L1, L2);
-  }
+  else
+    randomized_svd(A, M, N, lda, r, k, 16, L1, L2, dev);
 }
 
 }  // namespace host

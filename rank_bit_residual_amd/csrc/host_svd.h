@@ -16,9 +16,25 @@ void gemm(int64_t M, int64_t N, int64_t K, const TA* A, int64_t ars, int64_t acs
 // rotations, so that G_out = G_in * V.
 void jacobi_columns(double* G, int64_t m, int64_t n, int64_t ldg, double* V, int64_t ldv);
 
+// The two products of the randomized route with the fixed matrix A [M x N] (float32), for a
+// panel P of k float64 columns stored column-major (column c at P + c * len):
+//   kind 0: len = M, C^T = P^T A    -> C row-major [k x N];
+//   kind 1: len = N, C^T = P^T A^T  -> C row-major [k x M].
+// A backend runs them somewhere else (the GPU); it must return the products in float64.
+struct PanelProducts {
+  virtual ~PanelProducts() = default;
+  virtual void product(int kind, int64_t k, const double* P, double* C) = 0;
+};
+
 // Rank-r truncated SVD of A [M x N] (row stride lda): L1 [M x r] = U_r diag(sigma_r),
-// L2 [r x N] = V_r^T, both row-major contiguous, sigma descending.
-void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2);
+// L2 [r x N] = V_r^T, both row-major contiguous, sigma descending. With `dev`, the large
+// products of the randomized route run through it; the small dense steps stay on the host.
+void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2,
+                   PanelProducts* dev = nullptr);
+
+// Columns of the randomized route's panels for rank r of an M x N matrix (0: the full
+// Jacobi route is used and no panel products are needed).
+int64_t randomized_panel_columns(int64_t M, int64_t N, int64_t r);
 
 }  // namespace host
 }  // namespace svdq

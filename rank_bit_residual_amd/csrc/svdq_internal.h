@@ -59,6 +59,14 @@ struct LaunchPlan {
   int amax_blocks;           // amax_cols * amax_rows partial maxima
 };
 LaunchPlan make_plan(const Dims& d, int64_t B);
+
+// Truncated SVD with the randomized route's large products on the GPU (k_svd.hip): A [M x N]
+// float32 row-major on the host; workspace: device, >= device_panels_bytes(M, N, k) for
+// k = host::randomized_panel_columns(M, N, r); stream: a hipStream_t. Returns the first HIP
+// error (0 = none); small matrices take the host's full Jacobi route unchanged.
+size_t device_panels_bytes(int64_t M, int64_t N, int64_t k);
+int run_split_on_device(const float* A, int64_t M, int64_t N, int64_t r, void* workspace, void* stream, double* L1,
+                        double* L2);
 void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]);
 
 }  // namespace svdq

@@ -454,3 +454,31 @@ def test_linear_bias_exact_special_case():
     y = R.linear(_g(x, "f32"), p, bias=_g(bias, "f32"))
     want = x.astype(np.float64) @ w.astype(np.float64) + bias
     assert np.array_equal(_bits(_np(y)), _bits(want.astype(np.float32)))
+
+
+# ----------------------------------------------------------------------------- truncated SVD on the GPU
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prepare_with_gpu_svd(dtype):
+    """The randomized route's products on the GPU (float64): the split still meets the
+    Eckart-Young bound, matches the host route's factors' product, and the prepared operator
+    matches the oracle."""
+    rng = np.random.default_rng(24)
+    M, N, rank = 1024, 768, 32
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + (rng.standard_normal((M, 6)) * 0.3) @ rng.standard_normal((6, N)), dtype)
+    x = O.to_dtype(rng.standard_t(3, (64, M)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.5)
+    pg = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, 4, "int", keep_factors=True, svd_on_gpu=True)
+    ph = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, 4, "int", keep_factors=True)
+    ws = O.smooth_weight(w, s, dtype).astype(np.float64)
+    sig2 = np.sort(np.linalg.eigvalsh(ws.T @ ws))[::-1]
+    tail = np.sqrt(np.clip(sig2[rank:], 0, None).sum())
+    res = _np(pg.residual).astype(np.float64)
+    ulp = {"f32": 2.0**-24, "bf16": 2.0**-8}[dtype]
+    assert abs(np.linalg.norm(res) - tail) <= 1e-3 * tail + 4 * ulp * np.linalg.norm(ws)
+    prod_g = _np(pg.left).astype(np.float64) @ _np(pg.right).astype(np.float64)
+    prod_h = _np(ph.left).astype(np.float64) @ _np(ph.right).astype(np.float64)
+    assert O.rel_fro(prod_g, prod_h) <= (1e-5 if dtype == "f32" else 1e-2)
+    y = R.linear(_g(x, dtype), pg)
+    ref = O.forward_ref(x, s, _np(pg.left), _np(pg.right), _np(pg.residual), "int", 4, dtype)
+    assert O.rel_fro(_np(y), ref) <= TOL[dtype]
