@@ -259,26 +259,49 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + Q, 0xF, 0xF, false));
 }
 
+// The step's B operands of the down-projection (bf16 L1^T, tiled 16 rank columns x 128 K per
+// 2048 elements): lane (i, g) takes four 16-byte pieces per 16-column tile.
+template <int RC, class T>
+__device__ __forceinline__ void load_l1(const ActParams& p, const ActLane& L, int k0, v4i (&bw)[RC / 16][4]) {
+  const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
+#pragma unroll
+  for (int n = 0; n < RC / 16; n++)
+    if (n < L.nbl) {
+      const T* tile = l1t + ((int64_t)(L.rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + L.lane * (16 / sizeof(T));
+#pragma unroll
+      for (int c = 0; c < 4; c++) bw[n][c] = *reinterpret_cast<const v4i*>(tile + c * 512);
+    }
+}
+
+// Whether a full step's L1^T operands travel one step ahead with its x: with 16 rank columns
+// per block (16 registers); the 64-wide form would run out of registers, so it loads them at
+// the start of the step.
+constexpr bool l1_ahead(int RC) { return RC == 16; }
+
 // Inputs of a full bf16 step that the caller loads one step ahead: the lane's 32 x values
-// (16 words of bf16 pairs), two reciprocals and two scales. Lane l = 16 g + q holds RN(1/s)
-// and s of columns k0 + 2 l and k0 + 2 l + 1, i.e. the pair q of the block that the lanes of
-// row g work on.
+// (16 words of bf16 pairs), two reciprocals and two scales, and (l1_ahead) the step's L1^T
+// operands. Lane l = 16 g + q holds RN(1/s) and s of columns k0 + 2 l and k0 + 2 l + 1, i.e. the
+// pair q of the block that the lanes of row g work on.
+template <int RC>
 struct FullIn {
   u32 raw[16];
   float2 y2, s2;
+  v4i bw[l1_ahead(RC) ? RC / 16 : 1][4];
 };
 
-template <class T>
-__device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xrow, int lane, int g, int k0,
-                                          FullIn& in) {
-  const uint4* src = reinterpret_cast<const uint4*>(xrow + k0 + 32 * g);
+template <int RC, class T>
+__device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xrow, const ActLane& L, int k0,
+                                          FullIn<RC>& in) {
+  const uint4* src = reinterpret_cast<const uint4*>(xrow + k0 + 32 * L.g);
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const uint4 w = src[q];
     in.raw[4 * q] = w.x; in.raw[4 * q + 1] = w.y; in.raw[4 * q + 2] = w.z; in.raw[4 * q + 3] = w.w;
   }
-  in.y2 = *reinterpret_cast<const float2*>(p.recip + k0 + 2 * lane);
-  in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * lane);
+  in.y2 = *reinterpret_cast<const float2*>(p.recip + k0 + 2 * L.lane);
+  in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * L.lane);
+  if constexpr (l1_ahead(RC))
+    if (L.nbl > 0) load_l1<RC, T>(p, L, k0, in.bw);
 }
 
 // Full bf16 steps, exact path: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein,
@@ -289,8 +312,8 @@ __device__ __forceinline__ void load_full(const ActParams& p, const T* __restric
 // integer order is the numeric order).
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-template <int Q>
-__device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& amax16) {
+template <int Q, class IN>
+__device__ __forceinline__ void exact_pair(const IN& in, u32* xb, u16x2& amax16) {
   const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
   const float t0 = div_markstein(x0, row_bcast<Q>(in.s2.x), row_bcast<Q>(in.y2.x));
   const float t1 = div_markstein(x1, row_bcast<Q>(in.s2.y), row_bcast<Q>(in.y2.y));
@@ -298,8 +321,8 @@ __device__ __forceinline__ void exact_pair(const FullIn& in, u32* xb, u16x2& ama
   xb[Q] = pk;
   amax16 = __builtin_elementwise_max(amax16, __builtin_bit_cast(u16x2, pk & 0x7FFF7FFFu));
 }
-template <int... Q>
-__device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16) {
+template <class IN, int... Q>
+__device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, const IN& in, u32* xb, u16x2& amax16) {
   (exact_pair<Q>(in, xb, amax16), ...);
 }
 
@@ -309,8 +332,8 @@ __device__ __forceinline__ void exact_pairs(std::integer_sequence<int, Q...>, co
 // kept as a running minimum (packed 16-bit ops); the caller redoes the step exactly when any
 // lane of the wave saw one. (Products that underflow or overflow need no special case: near
 // zero the f32 error is far below the bf16 spacing, past the bf16 range both give inf.)
-template <int Q>
-__device__ __forceinline__ void fast_pair(const FullIn& in, u32* xb, u16x2& amax16, u16x2& band) {
+template <int Q, class IN>
+__device__ __forceinline__ void fast_pair(const IN& in, u32* xb, u16x2& amax16, u16x2& band) {
   const float x0 = __uint_as_float(in.raw[Q] << 16), x1 = __uint_as_float(in.raw[Q] & 0xFFFF0000u);
   const float t0 = x0 * row_bcast<Q>(in.y2.x), t1 = x1 * row_bcast<Q>(in.y2.y);
   const u32 pk = pack_bf16x2(t0, t1);
@@ -319,8 +342,8 @@ __device__ __forceinline__ void fast_pair(const FullIn& in, u32* xb, u16x2& amax
   const u32 lows = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);
   band = __builtin_elementwise_min(band, __builtin_bit_cast(u16x2, lows) + (u16x2){0x8003, 0x8003});
 }
-template <int... Q>
-__device__ __forceinline__ void fast_pairs(std::integer_sequence<int, Q...>, const FullIn& in, u32* xb, u16x2& amax16,
+template <class IN, int... Q>
+__device__ __forceinline__ void fast_pairs(std::integer_sequence<int, Q...>, const IN& in, u32* xb, u16x2& amax16,
                                            u16x2& band) {
   (fast_pair<Q>(in, xb, amax16, band), ...);
 }
@@ -346,7 +369,7 @@ struct StepState {
 // First half of a step: loads, X^ = D(x / scale) and its block maximum.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                           int k0, const FullIn& in, StepState<DT, RC>& st) {
+                                           int k0, const FullIn<RC>& in, StepState<DT, RC>& st) {
   typedef typename DT::T T;
   constexpr int RW = DT::is_bf16 ? 16 : 32;
   constexpr bool FAST = DT::is_bf16 && FULL;
@@ -371,17 +394,17 @@ __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT
     load_chan<FULL>(p.scale, k, p.M, 1.f, s32);
     load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
   }
-  // B operands of the down-projection for this step
+  // B operands of the down-projection for this step (bf16: with l1_ahead full steps got them
+  // one step ahead with x, other steps load them with their other loads; f32 loads them at the
+  // MFMAs to save registers)
   constexpr int NB = RC / 16;
-  // (bf16: loaded with the step's other loads; f32 loads them at the MFMAs to save registers)
-  if (DT::is_bf16 && L.nbl > 0) {
+  if constexpr (FAST && l1_ahead(RC)) {
 #pragma unroll
     for (int n = 0; n < NB; n++)
-      if (n < L.nbl) {
-        const T* tile = l1t + ((int64_t)(L.rbase / 16 + n) * (p.Kp / 128) + k0 / 128) * 2048 + L.lane * (16 / sizeof(T));
 #pragma unroll
-        for (int c = 0; c < 4; c++) bw[n][c] = *reinterpret_cast<const v4i*>(tile + c * 512);
-      }
+      for (int c = 0; c < 4; c++) bw[n][c] = in.bw[n][c];
+  } else if (DT::is_bf16 && L.nbl > 0) {
+    load_l1<RC, T>(p, L, k0, bw);
   }
 
   // X^ = D(x / scale); xb: X^ as stored (bf16 pairs or f32 bits); amax: max |X^| before the
@@ -475,23 +498,34 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
     else
       return __uint_as_float(xb[j]);
   };
-  // INT code of z: clamp(rint(RN_f32(z / s_x))). With the fast product t = RN(z * RN(1/s_x))
-  // (|t| <= qmax + 1, so 8 ulps < 2^-14) rint(t) is exact unless t lies within 2^-14 of a
-  // half-integer; those take the correctly rounded division.
-  const bool int_fast = L.ysx != 0.f;
-  auto int_code_of = [&](float z) -> int {
-    if (L.sx == 0.f) return 0;
-    float d;
+  // INT codes of the step's 32 values: clamp(rint(RN_f32(z / s_x))). The fast product
+  // t = RN(z * RN(1/s_x)) (|t| <= qmax + 1, so 8 ulps < 2^-14) rounds to the same integer
+  // unless it lies within 2^-14 of a half-integer; the largest distance to the nearest integer
+  // is kept, and when any lane of the wave saw one that close (or s_x has no stored
+  // reciprocal) the whole step takes the correctly rounded quotients. s_x = 0 (an all-zero
+  // tensor) gives code 0. The quotient is clamped to [-qmax, qmax] first (qmax is an integer,
+  // so this commutes with the rounding) and rounded by adding 1.5 * 2^23: the sum's low
+  // mantissa bits then hold the code, ties to even, in two's complement (tb[j]).
+  auto int_codes = [&](u32* tb) {
+    constexpr float SH = 0x1.8p23f;
+    const bool int_fast = L.ysx != 0.f;
+    float worst = 0.f;
     if (int_fast) {
-      d = z * L.ysx;
-      if (fabsf(d - __builtin_rintf(d)) >= 0.5f - 0x1p-14f) {
-        asm volatile("");  // rarely taken: keep it a branch
-        d = div_rn(z, L.sx, L.ysx);
+#pragma unroll
+      for (int j = 0; j < 32; j++) {
+        const float d = __builtin_amdgcn_fmed3f(val(j) * L.ysx, -L.qmax, L.qmax);
+        const float t = d + SH;
+        worst = fmaxf(worst, fabsf(d - (t - SH)));
+        tb[j] = __float_as_uint(t);
       }
-    } else {
-      d = div_rn(z, L.sx, L.ysx);
     }
-    return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(d), -L.qmax, L.qmax);
+    if (__any(!int_fast || worst >= 0.5f - 0x1p-14f)) {
+#pragma unroll
+      for (int j = 0; j < 32; j++) {
+        const float d = L.sx == 0.f ? 0.f : __builtin_amdgcn_fmed3f(div_rn(val(j), L.sx, L.ysx), -L.qmax, L.qmax);
+        tb[j] = __float_as_uint(d + SH);
+      }
+    }
   };
   if (L.do_codes && L.b < p.B) {
     if constexpr (FMT == SVDQ_FMT_MX) {
@@ -513,22 +547,26 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
       const int64_t si = p.mxs_tiled ? mx_scale_tiled_index(L.b, k / 32, p.Kp / 128) : (int64_t)L.b * p.lds + k / 32;
       p.mxs[si] = (uint8_t)(e + 127);
     } else if constexpr (NIB) {
+      u32 c[32];
+      int_codes(c);
       u32 ws[4];
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         u32 r = 0;
 #pragma unroll
-        for (int h = 0; h < 8; h++) r |= (u32)(int_code_of(val(8 * q + h)) & 0xF) << (4 * h);
+        for (int h = 0; h < 8; h++) r |= (c[8 * q + h] & 0xFu) << (4 * h);
         ws[q] = r;
       }
       *reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k / 2) = uint4{ws[0], ws[1], ws[2], ws[3]};
     } else {
+      u32 c[32];
+      int_codes(c);
       u32 ws[8];
 #pragma unroll
       for (int q = 0; q < 8; q++) {
         u32 r = 0;
 #pragma unroll
-        for (int h = 0; h < 4; h++) r |= (u32)(int_code_of(val(4 * q + h)) & 0xFF) << (8 * h);
+        for (int h = 0; h < 4; h++) r |= (c[4 * q + h] & 0xFFu) << (8 * h);
         ws[q] = r;
       }
       uint4* dst = reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k);
@@ -574,7 +612,7 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
 // reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                         int k0, v4f* acc, const FullIn& in) {
+                                         int k0, v4f* acc, const FullIn<RC>& in) {
   StepState<DT, RC> st;
   act_smooth<DT, FMT, NIB, FULL, RC>(p, xrow, L, k0, in, st);
   act_finish<DT, FMT, NIB, RC>(p, L, k0, acc, st);
@@ -597,22 +635,30 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   const int kend = kbeg + p.k_chunk_len < p.Kp ? kbeg + p.k_chunk_len : p.Kp;
   L.rbase = blockIdx.z * RC;
   L.nbl = p.rp > L.rbase ? ((p.rp - L.rbase) >= RC ? RC / 16 : (p.rp - L.rbase) / 16) : 0;
-  L.do_codes = blockIdx.z == 0 && p.codes != nullptr;
+  // The rank chunks of one (rows, K range) all smooth it; the codes are split between them by
+  // waves: waves 0-3 code in chunk 0 and waves 4-7 in chunk 1 (both in the only chunk when
+  // there is one), so a SIMD (waves s and s + 4) codes at most one step per round.
+  static_assert(NW == 8, "the code split below pairs waves s and s + 4 of a SIMD");
+  L.do_codes = p.codes != nullptr && (int)((wave / 4) % gridDim.z) == (int)blockIdx.z;
   const T* __restrict__ xrow = reinterpret_cast<const T*>(p.x) + (int64_t)bl * p.ldx;
+
+  // the first full bf16 step's x, scales and reciprocals are requested before the per-tensor
+  // maximum is read, so that the two memory round trips overlap
+  const int kfull = p.x_vec_ok ? p.M : 0;
+  int k0 = kbeg + 128 * wave;
+  FullIn<RC> cur;
+  const bool full0 = DT::is_bf16 && k0 < kend && k0 + 128 <= kfull;
+  if constexpr (DT::is_bf16)
+    if (full0) load_full<RC>(p, xrow, L, k0, cur);
 
   L.sx = 0.f;
   L.ysx = 0.f;
   L.qmax = 0.f;
   if constexpr (FMT == SVDQ_FMT_INT) {
+    // each wave reduces the partial maxima on its own (an exact max, so all waves agree)
     float a = 0.f;
-    for (int q = threadIdx.x; q < p.n_amax; q += 64 * NW) a = fmaxf(a, p.amax_part[q]);
-    a = wave_max(a);
-    __shared__ float shw[NW];
-    if (L.lane == 0) shw[wave] = a;
-    __syncthreads();
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < NW; q++) amax = fmaxf(amax, shw[q]);
+    for (int q = L.lane; q < p.n_amax; q += 64) a = fmaxf(a, p.amax_part[q]);
+    const float amax = wave_max(a);
     L.qmax = (float)((1 << (p.bits - 1)) - 1);
     L.sx = amax / L.qmax;
     L.ysx = (L.sx >= 0x1p-90f && L.sx <= 0x1p90f) ? 1.0f / L.sx : 0.f;
@@ -625,17 +671,13 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
 
   // full steps first (k0 ascending), then the tail and padding; bf16 full steps load the next
   // step's x and reciprocals before computing the current one
-  const int kfull = p.x_vec_ok ? p.M : 0;
-  int k0 = kbeg + 128 * wave;
-  FullIn cur;
   if constexpr (DT::is_bf16) {
-    if (k0 < kend && k0 + 128 <= kfull) {
-      load_full(p, xrow, L.lane, L.g, k0, cur);
+    if (full0) {
       for (;;) {
         const int kn = k0 + 128 * NW;
         const bool more = kn < kend && kn + 128 <= kfull;
-        FullIn nxt;
-        if (more) load_full(p, xrow, L.lane, L.g, kn, nxt);
+        FullIn<RC> nxt;
+        if (more) load_full<RC>(p, xrow, L, kn, nxt);
         act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur);
         k0 = kn;
         if (!more) break;
