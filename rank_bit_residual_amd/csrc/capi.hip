@@ -28,7 +28,9 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
   p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
   p.amax_cols = (int)ceil_div(d.M, 2048);
-  p.amax_rows = (int)std::min<int64_t>(65535, std::max<int64_t>(1, ceil_div(B, 8)));  // 8 rows per block
+  // 8 rows per block, fewer (down to 1) while that leaves under 256 blocks
+  const int64_t amax_rpb = std::max<int64_t>(1, std::min<int64_t>(8, B * p.amax_cols / 256));
+  p.amax_rows = (int)std::min<int64_t>(65535, std::max<int64_t>(1, ceil_div(B, amax_rpb)));
   p.amax_blocks = p.amax_cols * p.amax_rows;
   return p;
 }

@@ -9,6 +9,7 @@
 // conventions" items 1 and 3: smoothing divides x by scale; the low-rank branch takes the
 // unquantised smoothed activations; per-tensor INT with ties to even) and the msModelSlim
 // SVDQuant guide, step 2 (MXFP4 per-block minmax activations).
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -137,13 +138,14 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
   if (c0 < M) {
     int r = r0;
     if (DT::is_bf16 && vec_ok && c0 + 8 <= M) {
-      // eight rows per round, all loads issued before the maxima
-      for (; r + 8 <= r1; r += 8) {
-        uint4 w[8];
+      // rounds of U rows (8 while they last, then 4, 2, 1), all loads issued before the maxima
+      auto rows = [&](auto uc) {
+        constexpr int U = decltype(uc)::value;
+        uint4 w[U];
 #pragma unroll
-        for (int u = 0; u < 8; u++) w[u] = *reinterpret_cast<const uint4*>(x + (int64_t)(r + u) * ldx + c0);
+        for (int u = 0; u < U; u++) w[u] = *reinterpret_cast<const uint4*>(x + (int64_t)(r + u) * ldx + c0);
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
+        for (int u = 0; u < U; u++) {
           const u32 ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
           for (int h = 0; h < 4; h++) {
@@ -151,7 +153,12 @@ __global__ __launch_bounds__(256) void k_amax_cols(const typename DT::T* __restr
             cm[2 * h + 1] = fmaxf(cm[2 * h + 1], fabsf(__uint_as_float(ws[h] & 0xFFFF0000u)));
           }
         }
-      }
+        r += U;
+      };
+      while (r + 8 <= r1) rows(std::integral_constant<int, 8>());
+      if (r + 4 <= r1) rows(std::integral_constant<int, 4>());
+      if (r + 2 <= r1) rows(std::integral_constant<int, 2>());
+      if (r < r1) rows(std::integral_constant<int, 1>());
     }
     for (; r < r1; r++) {
       const typename DT::T* xr = x + (int64_t)r * ldx + c0;
