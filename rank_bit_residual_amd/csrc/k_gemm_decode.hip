@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int row = 16 * m + 4 * g + v;
-        if (row < p.B) y[(int64_t)row * p.ldy + col] = BF16::from_f32(acc[m][tt][v] + bz);
+        if (row < p.B) __builtin_nontemporal_store(BF16::from_f32(acc[m][tt][v] + bz), y + (int64_t)row * p.ldy + col);
       }
     }
 }

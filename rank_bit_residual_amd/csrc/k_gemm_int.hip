@@ -313,7 +313,8 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
     const T* src = tile + r * BN + cc * EPC;
     T* dst = y + (int64_t)row * p.ldy + c0;
     if (vec_ok && c0 + EPC <= p.N) {
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      // streaming store (the output is not read again by the operator)
+      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(src), reinterpret_cast<v4i*>(dst));
     } else {
       for (int e = 0; e < EPC && c0 + e < p.N; e++) dst[e] = src[e];
     }

@@ -353,7 +353,9 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const uint4 v = *reinterpret_cast<const uint4*>(tile + r * BN + cc * 8);
     T* dst = y + (int64_t)row * p.ldy + col;
     if (vec_ok && col + 8 <= p.N) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      // streaming store: the output is not read again here, so it should not push the operand
+      // stages that other tiles of this XCD still read out of L2
+      __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(dst));
     } else {
       const u32 w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
