@@ -128,6 +128,26 @@ def test_activation_codes_bit_exact_workloads(cid):
     _check_codes(x, s, wl.fmt, wl.bits, wl.dtype)
 
 
+@pytest.mark.parametrize("cid,B,rank", [(2, None, None), (5, None, None), (2, 48, 64), (5, 40, 96)])
+def test_linear_workspace_codes_bit_exact(cid, B, rank):
+    """The codes svdq_linear itself writes (white-box: its workspace begins with the
+    activation codes, row-major [B, Kp/2] nibbles) equal the oracle's. At these shapes the
+    activation kernel splits the rank over several blocks and shares the coding between
+    them, a path svdq_quantize_activations (one rank chunk) does not take."""
+    wl = WORKLOADS[cid]
+    x, w, s = make_inputs(cid, B=B)
+    rank = wl.rank if rank is None else rank
+    p = R.prepare(_g(w, wl.dtype), torch.from_numpy(s), rank, wl.bits, wl.fmt)
+    ws = torch.full((R.workspace_bytes(x.shape[0], p),), 0xA5, dtype=torch.uint8, device=dev())
+    R.linear(_g(x, wl.dtype), p, workspace=ws)
+    torch.cuda.synchronize()
+    want, _, _ = _act_codes_ref(x, s, wl.fmt, wl.bits, wl.dtype)
+    row = ((x.shape[1] + 255) // 256 * 256) // 2
+    got = ws[: x.shape[0] * row].cpu().numpy().reshape(x.shape[0], row)
+    assert np.array_equal(got[:, : want.shape[1]], want)
+    assert not got[:, want.shape[1]:].any()
+
+
 def test_int_linear_graph_replay_matches_eager():
     """The INT path (max pre-pass, activation kernel, INT4 GEMM) captured in a HIP graph:
     every replay must equal the eager result."""
