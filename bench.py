@@ -179,9 +179,10 @@ def run(args):
     # ---- timed region: eager launches. The library passes one HIP event pair to the
     # residual-GEMM dispatch of every EVERY-th call (stage 3 only): the roofline's kernel
     # duration comes from the timed calls themselves, while an event pair on every call
-    # (about 10 us of host time each) would make the loop host-bound.
+    # (about 10 us of host time each) would make the loop host-bound. EVERY is 16, or down to
+    # 8 for short runs, so that the average rests on a few dozen launches.
     GEMM_STAGE = 3
-    EVERY = 16
+    EVERY = max(8, min(16, args.steps // 50))
     L.check(lib.svdq_profile_begin_sampled(max(1, args.steps // EVERY + 1), 1 << GEMM_STAGE, EVERY))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -452,7 +453,7 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, wl, co
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=800)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="1 toy f32 INT4, 2 INT4 W4A4 bf16 (default), 3 MXFP4 DiT attention, 4 MXFP4 MLP up, "
