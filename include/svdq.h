@@ -46,7 +46,7 @@ typedef enum {
   SVDQ_OK = 0,
   SVDQ_EINVAL = 1,       /* invalid shape, stride, rank, bits, scale or buffer size */
   SVDQ_EDTYPE = 2,       /* unsupported dtype (e.g. float64) */
-  SVDQ_EUNSUPPORTED = 3, /* valid request this build does not implement */
+  SVDQ_EUNSUPPORTED = 3, /* a valid request this library does not implement */
   SVDQ_EHIP = 4          /* a HIP runtime call failed (launch error, bad device pointer) */
 } svdq_status;
 
