@@ -159,7 +159,10 @@ enum {
   SVDQ_NSEC = 7
 };
 
-/* Offsets of every section and the total size. Errors: EINVAL, EDTYPE. */
+/* Offsets of every section and the total size. Errors: EINVAL, EDTYPE, EUNSUPPORTED (INT
+ * formats whose residual products could leave int32: (M rounded up to 256) * qmax^2 * (256
+ * for bits <= 4, else 1) must be below 2^31, e.g. M <= 171008 at 4 bits, M <= 133120 at 8;
+ * the same rule holds for the svdq_prepare* calls and svdq_linear*). */
 int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
                          int64_t offsets[SVDQ_NSEC]);
 

@@ -108,14 +108,15 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-int check_linear_dims(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype) {
+// `gemm`: the shape also runs the residual GEMM (the INT int32-accumulation bound applies)
+int check_linear_dims(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype, bool gemm = true) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_format(fmt, bits))) return st;
   if (B < 1 || M < 1 || N < 1) return set_error(SVDQ_EINVAL, "B, M and N must be >= 1");
   if (B > kMaxDim || M > kMaxDim || N > kMaxDim) return set_error(SVDQ_EINVAL, "dimension too large");
   if (rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "rank must be in [0, min(M, N)]");
-  return SVDQ_OK;
+  return gemm ? check_int_accumulation(M, fmt, bits) : SVDQ_OK;
 }
 
 }  // namespace
@@ -128,7 +129,7 @@ extern "C" {
 int svdq_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t rank, int fmt, int bits, int dtype,
                          size_t* bytes_out) {
   clear_error();
-  int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
+  int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype, false);  // a size query (also for quantize_activations)
   if (st) return st;
   if (!bytes_out) return set_error(SVDQ_EINVAL, "bytes_out is NULL");
   const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
@@ -219,7 +220,7 @@ int svdq_quantize_activations(const void* x, int64_t B, int64_t M, int64_t ldx, 
                               void* workspace, size_t workspace_bytes, svdq_stream_t stream) {
   clear_error();
   clear_stale_hip_error();
-  int st = check_linear_dims(B, M, 1, 0, fmt, bits, dtype);
+  int st = check_linear_dims(B, M, 1, 0, fmt, bits, dtype, false);  // codes only, no residual GEMM
   if (st) return st;
   if (!x || !scale || !codes_out || !workspace) return set_error(SVDQ_EINVAL, "NULL buffer");
   if (fmt == SVDQ_FMT_MX && !scales_out) return set_error(SVDQ_EINVAL, "MX needs scales_out");

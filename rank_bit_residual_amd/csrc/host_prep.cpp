@@ -54,6 +54,17 @@ int check_format(int fmt, int bits) {
   return set_error(SVDQ_EINVAL, "unknown format code " + std::to_string(fmt));
 }
 
+int check_int_accumulation(int64_t M, int fmt, int bits) {
+  if (fmt != SVDQ_FMT_INT) return SVDQ_OK;
+  const int64_t qmax = ((int64_t)1 << (bits - 1)) - 1;
+  const int64_t prod = qmax * qmax * (bits <= 4 ? 256 : 1);
+  const int64_t Kp = (M + 255) / 256 * 256;
+  if (Kp > (((int64_t)1 << 31) - 1) / prod)
+    return set_error(SVDQ_EUNSUPPORTED, "INT residual: M too large for exact int32 accumulation (M rounded up to "
+                                        "256, times the largest code product, must stay below 2^31)");
+  return SVDQ_OK;
+}
+
 void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]) {
   int64_t o = 0;
   auto sec = [&](int id, int64_t bytes) {
@@ -161,7 +172,7 @@ int validate_prepare(int64_t M, int64_t N, int64_t ldw, int64_t rank, int fmt, i
   if (M < 1 || N < 1) return set_error(SVDQ_EINVAL, "weight must be a nonempty matrix");
   if (ldw < N) return set_error(SVDQ_EINVAL, "weight row stride smaller than N");
   if (rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "rank must be in [0, min(M, N)]");
-  return SVDQ_OK;
+  return check_int_accumulation(M, fmt, bits);
 }
 
 // Split ws [M,N] (float values exact in dtype) into rounded factors and the residual.

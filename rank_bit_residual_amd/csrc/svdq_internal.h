@@ -28,6 +28,10 @@ inline size_t dtype_size(int dtype) { return dtype == SVDQ_F32 ? 4 : 2; }
 // Validates (dtype, fmt, bits) and returns SVDQ_OK or the error status (message set).
 int check_dtype(int dtype);
 int check_format(int fmt, int bits);
+// INT residual products accumulate exactly in int32 on the matrix cores: Kp (M rounded up to
+// 256) times the largest code product (qmax^2, times 256 for 4-bit codes, which the int8
+// MFMAs see as 16 c) must stay below 2^31. EUNSUPPORTED otherwise (MX accumulates in fp32).
+int check_int_accumulation(int64_t M, int fmt, int bits);
 
 struct Dims {
   int64_t M, N, rank;

@@ -60,3 +60,27 @@ def test_host_calls_report_errors_without_a_gpu():
     assert b"every" in lib.svdq_last_error()
     n = ctypes.c_int()
     assert lib.svdq_profile_end(None, 0, ctypes.byref(n)) == _lib.SVDQ_EINVAL  # no open session
+
+
+def test_int_shapes_beyond_exact_int32_accumulation_are_refused():
+    """INT residual products accumulate in int32 on the matrix cores; shapes where
+    Kp * max|code product| could reach 2^31 (4-bit codes enter the int8 MFMAs as 16 c) are
+    refused with EUNSUPPORTED by preparation and the operator; MX (fp32 accumulation) and the
+    size query are unaffected."""
+    lib = _lib.load()
+    off = (ctypes.c_int64 * _lib.NSEC)()
+    # 4 bits: 256 * 7^2 = 12544 per product; 171008 * 12544 < 2^31 <= 171264 * 12544
+    assert lib.svdq_prepared_layout(171008, 64, 0, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_BF16, off) == _lib.SVDQ_OK
+    assert lib.svdq_prepared_layout(171009, 64, 0, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_BF16, off) == _lib.SVDQ_EUNSUPPORTED
+    assert b"int32" in lib.svdq_last_error()
+    # 8 bits (int8 codes as they are): 127^2 = 16129 per product
+    assert lib.svdq_prepared_layout(133120, 64, 0, _lib.SVDQ_FMT_INT, 8, _lib.SVDQ_F32, off) == _lib.SVDQ_OK
+    assert lib.svdq_prepared_layout(133121, 64, 0, _lib.SVDQ_FMT_INT, 8, _lib.SVDQ_F32, off) == _lib.SVDQ_EUNSUPPORTED
+    # 2 bits and MXFP4 are far from the bound
+    assert lib.svdq_prepared_layout(1 << 20, 64, 0, _lib.SVDQ_FMT_INT, 2, _lib.SVDQ_F32, off) == _lib.SVDQ_OK
+    assert lib.svdq_prepared_layout(1 << 20, 64, 0, _lib.SVDQ_FMT_MX, 4, _lib.SVDQ_BF16, off) == _lib.SVDQ_OK
+    # the operator refuses before touching any buffer; the size query still answers
+    assert lib.svdq_linear(None, 16, 200000, 200000, None, 64, 0, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_BF16,
+                           None, 64, None, 0, None) == _lib.SVDQ_EUNSUPPORTED
+    ws = ctypes.c_size_t()
+    assert lib.svdq_workspace_bytes(16, 200000, 64, 0, _lib.SVDQ_FMT_INT, 4, _lib.SVDQ_BF16, ctypes.byref(ws)) == 0
