@@ -12,6 +12,7 @@ records around its own launches), and the CPU oracle's throughput on a bounded s
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
        python bench.py --pmc-summary FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES
+       python bench.py --workload W --mfma-summary COUNTERS.csv
 """
 from __future__ import annotations
 
@@ -62,18 +63,29 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(wl, B):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; else None."""
+def _profile_summary(wl, B, suffix):
+    """A committed rocprofv3 counter summary of the GEMM for this workload, if it was taken on
+    the current kernel source; else None."""
     kname, src = gemm_kernel(wl, B)
-    path = os.path.join(ROOT, "profiles", f"{kname}_{wl.name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kname}_{wl.name}_{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha") != source_sha(src):
-        return None
-    return d.get("hbm_bytes_per_dispatch")
+    return d if d.get("source_sha") == source_sha(src) else None
+
+
+def pmc_traffic(wl, B):
+    """HBM bytes per GEMM launch from the committed counter summary, or None."""
+    d = _profile_summary(wl, B, "traffic")
+    return d.get("hbm_bytes_per_dispatch") if d else None
+
+
+def pmc_mfma_util(wl, B):
+    """MFMA utilisation of the GEMM (busy cycles / GPU-active cycles x SIMDs) from the committed
+    counter summary, or None."""
+    d = _profile_summary(wl, B, "mfma")
+    return d.get("mfma_util") if d else None
 
 
 def cpu_baseline(wl, x, s, prep, budget_s=10.0):
@@ -250,6 +262,8 @@ def run(args):
         ach = work["gemm_bytes"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]}
     roof["traffic"] = traffic
+    if roof["bound"] == "mfma":
+        roof["mfma_util"] = pmc_mfma_util(wl, B)  # counter evidence: MFMA busy / active cycles
     roof["kernel"] = gemm_kernel(wl, B)[0]
     roof["avg_ms"] = gemm_ms
     roof["algorithmic_bytes"] = work["gemm_bytes"]
@@ -450,6 +464,34 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, wl, co
     print(json.dumps(d, indent=1))
 
 
+def mfma_summary(csv_path, wl, command):
+    """MFMA utilisation of the residual GEMM from one rocprofv3 counter CSV holding
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE (with --kernel-trace):
+    busy cycles summed over the SIMDs / (GPU-active cycles of one XCC x SIMDs), the same
+    definition as rocprof's MfmaUtil. GRBM_GUI_ACTIVE is summed over the XCCs in the CSV."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            k = row.get("Kernel_Name", "")
+            kname, _ = gemm_kernel(wl, wl.B)
+            if (kname + "<") not in k and (kname + "(") not in k:
+                continue
+            d = per.setdefault(row["Dispatch_Id"], {})
+            d[row["Counter_Name"]] = float(row["Counter_Value"])
+            d["ns"] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    ds = [d for d in per.values() if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA"} <= d.keys()]
+    n = len(ds)
+    avg = lambda key: sum(d[key] for d in ds) / n  # noqa: E731
+    xcc, simds = 8, 1024
+    busy, gui, inst, ns = avg("SQ_VALU_MFMA_BUSY_CYCLES"), avg("GRBM_GUI_ACTIVE") / xcc, avg("SQ_INSTS_MFMA"), avg("ns")
+    kname, src = gemm_kernel(wl, wl.B)
+    print(json.dumps({"kernel": kname, "workload": wl.name, "source_sha": source_sha(src), "dispatches": n,
+                      "mfma_instructions": inst, "mfma_busy_cycles": busy, "gpu_active_cycles_per_xcc": gui,
+                      "dispatch_ns": ns, "mfma_util": busy / (gui * simds),
+                      "mfma_busy_fraction_at_2400MHz": busy / (simds * ns * 2.4), "command": command}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -462,6 +504,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_BYTES"))
+    ap.add_argument("--mfma-summary", metavar="CSV", help="MFMA utilisation of the GEMM from a counter CSV")
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--toy-experiment", action="store_true",
                     help="run the exercise page's toy experiment through the library and print its error table")
@@ -472,6 +515,11 @@ def main():
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.mfma_summary:
+        from workloads import WORKLOADS
+
+        mfma_summary(args.mfma_summary, WORKLOADS[args.workload], args.pmc_command)
+        return 0
     if args.pmc_summary:
         from workloads import WORKLOADS
 
