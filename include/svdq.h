@@ -147,6 +147,9 @@ int svdq_fake_quantize(const void* z, int64_t rows, int64_t cols, int64_t szr, i
  *   SVDQ_SEC_L2T     dtype [Np, rp]    L2^T (up-projection factor, transposed)
  *   SVDQ_SEC_RECIP   float32 [M]       RN(1/scale[m]), or 0 where scale[m] lies outside
  *                    [2^-90, 2^90]; the kernels use it for an exact fast x / scale
+ *   SVDQ_SEC_GLOBAL  float32 [4]       MX two-level scaling (svdq_prepare_two_level):
+ *                    {g_x, g_R, alpha, 0}, the activation and residual global scales and
+ *                    alpha = RN(1 / (g_x g_R)); {1, 1, 1, 0} for every other preparation
  * ------------------------------------------------------------------------------------ */
 enum {
   SVDQ_SEC_SCALE = 0,
@@ -155,8 +158,9 @@ enum {
   SVDQ_SEC_L1T = 3,
   SVDQ_SEC_L2T = 4,
   SVDQ_SEC_RECIP = 5,
-  SVDQ_SEC_END = 6, /* offsets[SVDQ_SEC_END] = total blob bytes */
-  SVDQ_NSEC = 7
+  SVDQ_SEC_GLOBAL = 6,
+  SVDQ_SEC_END = 7, /* offsets[SVDQ_SEC_END] = total blob bytes */
+  SVDQ_NSEC = 8
 };
 
 /* Offsets of every section and the total size. Errors: EINVAL, EDTYPE, EUNSUPPORTED (INT
@@ -194,6 +198,23 @@ int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, cons
                      int64_t rank, int fmt, int bits, int dtype, void* blob_host,
                      void* left_out, void* right_out, void* residual_out,
                      void* workspace, size_t workspace_bytes, svdq_stream_t stream);
+
+/* MXFP4 with two-level scaling ([FI] svdquant_linear: an activation global scale and a
+ * per-tensor residual scale alpha over the block scales, with the low-rank up-projection
+ * factor prepared divided by alpha, [FI]'s l1_scaled, so that the epilogue applies alpha
+ * once; that factor is L2 in this library's notation): the residual is quantised
+ * as z_R = RN(R * g_R), E8M0 per 32-block of z_R, where g_R = RN(6 * 2^ex / max|R|) with
+ * max|R| / 6 = f * 2^ex, f in [0.5, 1) (so g_R lies in (1, 2] and the largest |z_R| is 6 * 2^ex
+ * up to rounding; g_R = 1 for an all-zero R); each call quantises the activations as
+ * z_x = RN(X^ * g_x) with the caller's x_global_scale g_x (finite, in [2^-64, 2^64]; a value
+ * calibrated offline, as the residual's); alpha = RN(1 / (g_x g_R)) in binary64, and the blob
+ * holds D(L2^T / alpha) in SVDQ_SEC_L2T. svdq_linear then computes
+ * Y = D(alpha * (Q(z_x) Q(z_R) + down (L2^T / alpha)^T) [+ bias]). left_out, right_out,
+ * residual_out receive the unscaled factors and R as svdq_prepare's do. fmt is SVDQ_FMT_MX,
+ * bits 4. Errors as svdq_prepare, plus EINVAL for x_global_scale outside the range. */
+int svdq_prepare_two_level(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
+                           int64_t rank, float x_global_scale, int dtype, void* blob_host,
+                           void* left_out, void* right_out, void* residual_out);
 
 /* The same preparation from a weight in the Linear layout ([FI] Parameters: the weight as
  * [n, k], output channels by input channels): weight_nm is [N, M] with host row stride

@@ -7,6 +7,9 @@ Sources (cited by page title and section):
        (recommended YAML: MXFP4, per_block, symmetric, minmax for act and weight).
   [P5] "Contraction-Gauge Preconditioning for Quantized Matrix Multiplication",
        abstract: the product identity AB = (AT)(T^-1 B).
+  [P2] "flashinfer.gemm.svdquant_linear" (API page): the activation global scale, the
+       per-tensor residual dequantisation scale alpha and the up-projection factor
+       prepared divided by alpha (its l1_scaled parameter).
 
 Precision conventions (readings where the pages are silent; each one is listed
 in the design notes):
@@ -23,6 +26,7 @@ arrays holding bf16-representable values.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -251,7 +255,8 @@ def pack_int_codes(codes, bits: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- the operator
-def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str, bias=None) -> np.ndarray:
+def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str, bias=None,
+                x_global_scale=None) -> np.ndarray:
     """[P1] "Formula and conventions" item 3, Y = (X^ L1) L2 + Q(X^) Q(R), in float64, plus an
     optional per-output-channel bias [N] (the GPU library page's optional bias parameter).
 
@@ -259,7 +264,14 @@ def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str
     factors; only R is quantised on the weight side. fmt "int": per-tensor INT
     (s_x * s_R * integer product, exact); fmt "mx": MXFP4 along K for X^ rows and
     R columns ([P4] per_block), the product of exactly dequantised values.
+
+    ``x_global_scale`` (fmt "mx" only) selects two-level scaling, [P2]'s chain: see
+    forward_two_level.
     """
+    if x_global_scale is not None:
+        if fmt != "mx":
+            raise ValueError("two-level scaling is an MXFP4 scheme")
+        return forward_two_level(x, scale, left, right, residual, dtype, x_global_scale, bias)
     xs = smooth_activations(x, scale, dtype)
     low = (np.asarray(xs, np.float64) @ np.asarray(left, np.float64)) @ np.asarray(right, np.float64)
     if fmt == "int":
@@ -275,6 +287,70 @@ def forward_ref(x, scale, left, right, residual, fmt: str, bits: int, dtype: str
     else:
         raise ValueError(f"unknown format {fmt!r}")
     y = low + res
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
+
+
+# --------------------------------------------------------------------------- two-level MXFP4 scaling
+def two_level_residual_scale(residual) -> np.float32:
+    """Residual global scale g_R (a reading: [P2] names a per-tensor residual dequantisation
+    scale but not how it is chosen). With max|R| / 6 in [2^(ex-1), 2^ex), g_R is
+    6 * 2^ex / max|R| rounded once to binary32, so g_R lies in (1, 2] and the largest
+    |R * g_R| sits at 6 * 2^ex: the top E2M1 value at its block's scale. An all-zero R
+    takes g_R = 1.
+
+    ex comes from exact rational comparisons; float(Fraction) rounds the exact quotient to
+    binary64 and the second rounding to binary32 cannot differ from a direct one, since a
+    quotient of two 24-bit significands rounded to 53 bits and then to 24 is correctly
+    rounded (Figueroa's double-rounding condition 53 >= 2 * 24 + 2).
+    """
+    r = np.asarray(residual, np.float64)
+    a = Fraction(float(np.max(np.abs(r)))) if r.size else Fraction(0)
+    if a == 0:
+        return np.float32(1.0)
+    q = a / 6
+    ex = 0
+    while Fraction(2) ** ex <= q:
+        ex += 1
+    while Fraction(2) ** (ex - 1) > q:
+        ex -= 1
+    return np.float32(float(6 * Fraction(2) ** ex / a))
+
+
+def two_level_alpha(x_global_scale, g_resid) -> np.float32:
+    """[P2] alpha, the per-tensor dequantisation scale of the quantised product: the
+    reciprocal of g_x * g_R, taken in binary64 (the product of two binary32 numbers is exact
+    there) and rounded once to binary32 (a reading: the page leaves the rounding open)."""
+    return np.float32(1.0 / (float(np.float32(x_global_scale)) * float(np.float32(g_resid))))
+
+
+def forward_two_level(x, scale, left, right, residual, dtype: str, x_global_scale, bias=None) -> np.ndarray:
+    """[P2] svdquant_linear's three steps with MXFP4 in place of NVFP4, in float64:
+
+      1. X^ = D(x/scale), z_x = RN_f32(X^ * g_x), MXFP4 codes of z_x along K;
+      2. down = X^ L1 (the unquantised low-rank input);
+      3. Y = alpha * (Q(z_x) Q(z_R) + down * D(L2 / alpha)) [+ bias],
+
+    where z_R = RN_f32(R * g_R) is quantised per column of R along K, g_R and alpha are as in
+    two_level_residual_scale and two_level_alpha, and D(L2 / alpha) is the up-projection
+    factor divided by alpha and rounded to the storage dtype, as [P2] prepares l1_scaled.
+    Both products are sums of exactly dequantised values taken in float64.
+    """
+    if dtype == "f64":
+        raise ValueError("two-level scaling quantises binary32 products; use f32 or bf16")
+    gx = np.float32(x_global_scale)
+    gr = two_level_residual_scale(residual)
+    alpha = two_level_alpha(gx, gr)
+    xs = smooth_activations(x, scale, dtype)
+    zx = np.asarray(xs, np.float32) * gx
+    zr = np.asarray(residual, np.float32) * gr
+    cx, bx = quantize_mx(zx)
+    cr, br = quantize_mx(zr.T)
+    acc = dequant_mx(cx, bx) @ dequant_mx(cr, br).T
+    down = np.asarray(xs, np.float64) @ np.asarray(left, np.float64)
+    up = np.asarray(to_dtype(np.asarray(right, np.float64) / float(alpha), dtype), np.float64)
+    y = float(alpha) * (acc + down @ up)
     if bias is not None:
         y = y + np.asarray(bias, np.float64)[None, :]
     return y

@@ -35,6 +35,8 @@ SIGNATURES = {
     "svdq_prepare_gpu_workspace_bytes": (c_int, [c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "svdq_prepare_gpu": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_sz, c_vp]),
+    "svdq_prepare_two_level": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, ctypes.c_float, c_int, c_vp, c_vp,
+                                       c_vp, c_vp]),
     "svdq_prepare_linear": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "svdq_calibrate_workspace_bytes": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "svdq_calibrate_scale": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, ctypes.c_double, c_vp, c_vp,
@@ -49,8 +51,8 @@ STAGE_NAMES = ("amax", "act_quant_down", "down_reduce", "gemm")
 SVDQ_OK, SVDQ_EINVAL, SVDQ_EDTYPE, SVDQ_EUNSUPPORTED, SVDQ_EHIP = 0, 1, 2, 3, 4
 SVDQ_F32, SVDQ_BF16, SVDQ_F64 = 0, 1, 2
 SVDQ_FMT_INT, SVDQ_FMT_MX = 0, 1
-SEC_SCALE, SEC_RCODES, SEC_RSCALES, SEC_L1T, SEC_L2T, SEC_RECIP, SEC_END = 0, 1, 2, 3, 4, 5, 6
-NSEC = 7
+SEC_SCALE, SEC_RCODES, SEC_RSCALES, SEC_L1T, SEC_L2T, SEC_RECIP, SEC_GLOBAL, SEC_END = 0, 1, 2, 3, 4, 5, 6, 7
+NSEC = 8
 
 _lib = None
 

@@ -194,14 +194,18 @@ def prepared_layout(M: int, N: int, rank: int, fmt: str = "int", bits: int = 4, 
 
 
 def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4, fmt: str = "int",
-            device=None, keep_factors: bool = False, layout: str = "mn", svd_on_gpu: bool = False) -> Prepared:
+            device=None, keep_factors: bool = False, layout: str = "mn", svd_on_gpu: bool = False,
+            x_global_scale: float | None = None) -> Prepared:
     """One-time preparation: fold scale into W, split, quantise and pack the residual (host),
     then copy the blob to ``device`` (default: the weight's device, which must be a GPU).
 
     ``layout="mn"`` takes W as [M, N] (input by output channels); ``layout="nm"`` takes a
     Linear-layout weight [N, M] (output by input channels, i.e. W transposed) without a copy
     into the other orientation; both give the same blob. ``svd_on_gpu`` runs the truncated
-    SVD's large products on ``device`` (layout "mn" only)."""
+    SVD's large products on ``device`` (layout "mn" only). ``x_global_scale`` (MXFP4, layout
+    "mn", host SVD) selects two-level scaling: the activations are quantised as
+    RN(X^ * x_global_scale), the residual with its own global scale, and alpha applies once
+    in the GEMM epilogue (svdq_prepare_two_level)."""
     if layout not in ("mn", "nm"):
         raise ValueError('layout must be "mn" ([M, N]) or "nm" (Linear layout [N, M])')
     if weight.dim() != 2 or scale.dim() != 1:
@@ -224,7 +228,12 @@ def prepare(weight: torch.Tensor, scale: torch.Tensor, rank: int, bits: int = 4,
         res = torch.empty((M, N), dtype=weight.dtype)
     dev = weight.device if device is None else torch.device(device)
     outs = (_ptr(left) if keep_factors and rank else None, _ptr(right) if keep_factors and rank else None, _ptr(res))
-    if svd_on_gpu:
+    if x_global_scale is not None:
+        if fmt != "mx" or layout != "mn" or svd_on_gpu:
+            raise ValueError("x_global_scale (two-level scaling) needs fmt 'mx', layout 'mn' and the host SVD")
+        L.check(lib.svdq_prepare_two_level(_ptr(host_w), M, N, N, _ptr(host_s), rank, float(x_global_scale), code,
+                                           _ptr(blob), *outs))
+    elif svd_on_gpu:
         if layout != "mn" or dev.type != "cuda":
             raise ValueError("svd_on_gpu needs layout 'mn' and a GPU device")
         need = ctypes.c_size_t()
@@ -251,7 +260,8 @@ def workspace_bytes(B: int, prep: Prepared) -> int:
 
 def linear(x: torch.Tensor, prep: Prepared, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, bias: torch.Tensor | None = None) -> torch.Tensor:
-    """The per-call operator Y = (X^ L1) L2 + Q(X^) Q(R) (+ bias[N]) on prepared weights."""
+    """The per-call operator Y = (X^ L1) L2 + Q(X^) Q(R) (+ bias[N]) on prepared weights
+    (with two-level MXFP4 weights: Y = alpha (Q(X^ g_x) Q(R g_R) + (X^ L1) L2 / alpha) (+ bias))."""
     _require_gpu(x, prep.blob)
     if prep.blob.device != x.device:
         raise ValueError("x and the prepared weights must be on the same device")

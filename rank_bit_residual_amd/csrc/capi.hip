@@ -339,6 +339,8 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   p.k_chunks = pl.k_chunks;
   p.k_chunk_len = pl.k_chunk_len;
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
+  const float* glob = (const float*)(bl + boff[SVDQ_SEC_GLOBAL]);  // {g_x, g_R, alpha, 0}
+  if (fmt == SVDQ_FMT_MX) p.gscale = glob;
   tm.begin(1);
   if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, pl.rchunk, s), "activation quantise launch")))
     return st;
@@ -362,6 +364,7 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   g.rp = (int)d.rp;
   g.y = y;
   g.bias = bias;
+  if (fmt == SVDQ_FMT_MX) g.alpha = glob + 2;
   g.ldy = ldy;
   g.B = (int)B;
   g.N = (int)N;

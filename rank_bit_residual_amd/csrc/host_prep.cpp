@@ -77,6 +77,7 @@ void blob_layout(const Dims& d, int64_t off[SVDQ_NSEC]) {
   sec(SVDQ_SEC_L1T, d.rp * d.Kp * (int64_t)dtype_size(d.dtype));
   sec(SVDQ_SEC_L2T, d.Np * d.rp * (int64_t)dtype_size(d.dtype));
   sec(SVDQ_SEC_RECIP, d.M * 4);
+  sec(SVDQ_SEC_GLOBAL, 16);
   off[SVDQ_SEC_END] = o;
 }
 
@@ -266,7 +267,7 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
 
 static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
                         int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out,
-                        SplitDevice* dev = nullptr);
+                        SplitDevice* dev = nullptr, float x_gscale = 0.f);
 
 int svdq_prepare_gpu_workspace_bytes(int64_t M, int64_t N, int64_t rank, size_t* bytes_out) {
   clear_error();
@@ -306,6 +307,19 @@ int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const fl
                       right_out, residual_out);
 }
 
+int svdq_prepare_two_level(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale, int64_t rank,
+                           float x_global_scale, int dtype, void* blob_host, void* left_out, void* right_out,
+                           void* residual_out) {
+  clear_error();
+  int st = validate_prepare(M, N, ldw, rank, SVDQ_FMT_MX, 4, dtype);
+  if (st) return st;
+  if (!weight || !scale || !blob_host) return set_error(SVDQ_EINVAL, "NULL buffer passed to prepare");
+  if (!(x_global_scale >= 0x1p-64f && x_global_scale <= 0x1p64f))
+    return set_error(SVDQ_EINVAL, "x_global_scale must be finite and in [2^-64, 2^64]");
+  return prepare_impl(HostMat{weight, ldw, dtype, false}, M, N, scale, rank, SVDQ_FMT_MX, 4, dtype, blob_host,
+                      left_out, right_out, residual_out, nullptr, x_global_scale);
+}
+
 int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw, const float* scale, int64_t rank,
                         int fmt, int bits, int dtype, void* blob_host, void* left_out, void* right_out,
                         void* residual_out) {
@@ -319,9 +333,11 @@ int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw
                       right_out, residual_out);
 }
 
+// x_gscale > 0: MX two-level scaling with that activation global scale (see
+// svdq_prepare_two_level); 0: plain preparation (SVDQ_SEC_GLOBAL = {1, 1, 1, 0}).
 static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* scale, int64_t rank, int fmt, int bits,
                         int dtype, void* blob_host, void* left_out, void* right_out, void* residual_out,
-                        SplitDevice* dev) {
+                        SplitDevice* dev, float x_gscale) {
   int st;
   if ((st = svdq_check_smoothing(1, M, M, M, N, scale))) return st;
   const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
@@ -349,6 +365,24 @@ static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* sca
     }
   }
 
+  // two-level scaling (MX): the residual's global scale g_R maps max|R| onto 6 * 2^ex (see
+  // svdq_prepare_two_level), alpha = RN(1 / (g_x g_R)) in binary64
+  float g_resid = 1.f, alpha = 1.f;
+  if (x_gscale > 0.f) {
+    float a = 0.f;
+    for (float v : R) a = std::max(a, std::fabs(v));
+    if (a > 0.f) {
+      int ex = 0;
+      (void)std::frexp((double)a / 6.0, &ex);
+      g_resid = (float)(std::ldexp(6.0, ex) / (double)a);
+    }
+    alpha = (float)(1.0 / ((double)x_gscale * (double)g_resid));
+  }
+  {
+    const float gl[4] = {x_gscale > 0.f ? x_gscale : 1.f, g_resid, alpha, 0.f};
+    std::memcpy(blob + off[SVDQ_SEC_GLOBAL], gl, sizeof gl);
+  }
+
   uint8_t* codes = blob + off[SVDQ_SEC_RCODES];
   const int64_t crow = d.code_row_bytes();
   if (fmt == SVDQ_FMT_INT) {
@@ -372,7 +406,9 @@ static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* sca
       }
     }
   } else {
-    // MXFP4 per column n of R, 32-element blocks along m
+    // MXFP4 per column n of z = RN(R * g_R) (g_R = 1 without two-level scaling), 32-element
+    // blocks along m
+    const float gr = g_resid;
     uint8_t* sc = blob + off[SVDQ_SEC_RSCALES];
     const int64_t nb = ceil_div(M, kMxBlock);
 #pragma omp parallel for schedule(static)
@@ -380,11 +416,11 @@ static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* sca
       for (int64_t b = 0; b < nb; b++) {
         const int64_t m0 = b * kMxBlock, m1 = std::min(M, m0 + kMxBlock);
         float a = 0.f;
-        for (int64_t m = m0; m < m1; m++) a = std::max(a, std::fabs(R[m * N + n]));
+        for (int64_t m = m0; m < m1; m++) a = std::max(a, std::fabs(R[m * N + n] * gr));
         const int e = mx_exponent(a);
         sc[mx_tiled(n, b, d.Kp / 128)] = (uint8_t)(e + 127);
         for (int64_t m = m0; m < m1; m++)
-          codes[mx_code_tiled(n, m / 2, d.Kp / 128)] |= (uint8_t)(e2m1_code(R[m * N + n], e) << (4 * (m & 1)));
+          codes[mx_code_tiled(n, m / 2, d.Kp / 128)] |= (uint8_t)(e2m1_code(R[m * N + n] * gr, e) << (4 * (m & 1)));
       }
     }
   }
@@ -399,8 +435,12 @@ static int prepare_impl(const HostMat& W, int64_t M, int64_t N, const float* sca
       const int64_t in_tile = ((((m % 32) / E) * 4 + (m % 128) / 32) * 16 + t % 16) * E + m % E;
       store_exact(l1t, tile * 2048 + in_tile, dtype, L1[m * rank + t]);
     }
+  // (two-level: the up-projection factor divided by alpha, rounded to the dtype)
   for (int64_t n = 0; n < N; n++)
-    for (int64_t t = 0; t < rank; t++) store_exact(l2t, n * d.rp + t, dtype, L2[t * N + n]);
+    for (int64_t t = 0; t < rank; t++) {
+      const float v = alpha == 1.f ? L2[t * N + n] : round_f64((double)L2[t * N + n] / (double)alpha, dtype);
+      store_exact(l2t, n * d.rp + t, dtype, v);
+    }
 
   if (left_out)
     for (int64_t i = 0; i < M * rank; i++) store_exact(left_out, i, dtype, L1[i]);

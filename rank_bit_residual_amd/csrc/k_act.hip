@@ -257,6 +257,7 @@ struct ActLane {
   int lane, i, g, b, rbase, nbl;
   bool do_codes;
   float sx, ysx, qmax;
+  float gx;  // MX two-level scaling: codes of RN(X^ g_x) (1 when not scaled)
 };
 
 // Broadcast of lane Q of each 16-lane row to the whole row (DPP row_newbcast; the compiler
@@ -536,17 +537,20 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
   };
   if (L.do_codes && L.b < p.B) {
     if constexpr (FMT == SVDQ_FMT_MX) {
-      const int e = mx_exponent(amax);
+      // two-level scaling quantises z = RN(X^ g_x): the block maximum of |z| is RN(amax g_x)
+      // (a positive scale and the rounding are monotone)
+      const bool scaled = L.gx != 1.f;
+      const int e = mx_exponent(scaled ? amax * L.gx : amax);
       const float sc = pow2f(e);
       u32 w4[4];
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        if constexpr (DT::is_bf16) {
+        if (DT::is_bf16 && !scaled) {
           w4[q] = fp4_pack8_bf16(&xb[4 * q], sc);
         } else {
           float v[8];
 #pragma unroll
-          for (int h = 0; h < 8; h++) v[h] = val(8 * q + h);
+          for (int h = 0; h < 8; h++) v[h] = val(8 * q + h) * L.gx;
           w4[q] = fp4_pack8(v, sc);
         }
       }
@@ -661,6 +665,7 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   L.sx = 0.f;
   L.ysx = 0.f;
   L.qmax = 0.f;
+  L.gx = (FMT == SVDQ_FMT_MX && p.gscale) ? p.gscale[0] : 1.f;
   if constexpr (FMT == SVDQ_FMT_INT) {
     // each wave reduces the partial maxima on its own (an exact max, so all waves agree)
     float a = 0.f;

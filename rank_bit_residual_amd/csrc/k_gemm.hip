@@ -238,6 +238,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       }
     }
   }
+  if (p.alpha) {  // two-level MX scaling: alpha * (residual + down L2 / alpha)
+    const float al = p.alpha[0];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) f[mt][nt][v] *= al;
+  }
   T* y = reinterpret_cast<T*>(p.y);
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {

@@ -216,6 +216,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
         acc[m][tt][v] = sum;
       }
 
+  const float al = p.alpha ? p.alpha[0] : 1.f;  // two-level MX scaling (applied before the bias)
   T* y = reinterpret_cast<T*>(p.y);
 #pragma unroll
   for (int m = 0; m < MT; m++)
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int row = 16 * m + 4 * g + v;
-        if (row < p.B) __builtin_nontemporal_store(BF16::from_f32(acc[m][tt][v] + bz), y + (int64_t)row * p.ldy + col);
+        if (row < p.B) __builtin_nontemporal_store(BF16::from_f32(acc[m][tt][v] * al + bz), y + (int64_t)row * p.ldy + col);
       }
     }
 }

@@ -304,6 +304,17 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   stage(nst - 2, fa, sa, fb, sb, LastButOne());
   stage(nst - 1, fb, sb, fa, sa, Last());
 
+  // ---- two-level scaling: alpha * (residual + down L2 / alpha), before the bias
+  if (p.alpha) {
+    const float al = p.alpha[0];
+#pragma unroll
+    for (int i = 0; i < C::MT; i++)
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[i][j][v] *= al;
+  }
+
   // ---- output bias (one column per lane and 32x32 tile)
   if (p.bias) {
 #pragma unroll

@@ -29,6 +29,7 @@ struct ActParams {
   void* down;        // [B][rp] dtype when k_chunks == 1
   int k_chunks, k_chunk_len;
   int x_vec_ok;  // x base and row stride allow 16-byte loads
+  const float* gscale;  // MX: the activation global scale g_x (codes of RN(X^ g_x)), or NULL
 };
 
 struct GemmParams {
@@ -50,6 +51,7 @@ struct GemmParams {
   void* y;
   int64_t ldy;
   const void* bias;  // [N] dtype added before the output rounding, or nullptr
+  const float* alpha;  // MX: residual-plus-up-projection scale applied before the bias, or nullptr
   int B, N, kstages;
   int npad;  // rows of the prepared weight (N rounded up); loads clamp to npad - 1
 };

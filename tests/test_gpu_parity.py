@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import rank_bit_residual_amd as R
+from rank_bit_residual_amd import _lib
 from oracle import svdquant as O
 from workloads import WORKLOADS, make_inputs
 
@@ -502,3 +503,84 @@ def test_prepare_with_gpu_svd(dtype):
     y = R.linear(_g(x, dtype), pg)
     ref = O.forward_ref(x, s, _np(pg.left), _np(pg.right), _np(pg.residual), "int", 4, dtype)
     assert O.rel_fro(_np(y), ref) <= TOL[dtype]
+
+
+# ----------------------------------------------------------------------------- two-level MXFP4 scaling
+def _two_level_case(B, M, N, rank, dtype, gx, seed, bias=False):
+    rng = np.random.default_rng(seed)
+    x = O.to_dtype(rng.standard_t(3, (B, M)), dtype)
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 3)) @ rng.standard_normal((3, N)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.25)
+    b = O.to_dtype(rng.standard_normal(N), dtype) if bias else None
+    p = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, 4, "mx", keep_factors=True, x_global_scale=gx)
+    y = R.linear(_g(x, dtype), p, bias=None if b is None else _g(b, dtype))
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "mx", 4, dtype, bias=b, x_global_scale=gx)
+    return O.rel_fro(_np(y), ref)
+
+
+@pytest.mark.parametrize("B,M,N,rank,dtype,gx,bias", [
+    (512, 512, 576, 32, "bf16", 1.37, False),   # large-batch kernel
+    (300, 1024, 392, 0, "bf16", 0.011, True),   # large-batch kernel, rank 0, bias
+    (16, 1024, 200, 48, "bf16", 5.5, True),     # decode kernel, bias
+    (33, 4352, 300, 128, "bf16", 0.7, False),   # decode kernel, split-K partials
+    (100, 640, 300, 32, "bf16", 1.37, False),   # general kernel (64 < B < 256)
+    (40, 320, 130, 16, "f32", 3.1, True),       # general kernel, float32 io
+])
+def test_two_level_parity(B, M, N, rank, dtype, gx, bias):
+    err = _two_level_case(B, M, N, rank, dtype, gx, B + N, bias)
+    print(f"two-level B={B} M={M} N={N} rank={rank} {dtype}: rel Frobenius error {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("cid,rows", [(3, 256), (5, None)])
+def test_two_level_parity_workloads(cid, rows):
+    wl = WORKLOADS[cid]
+    x, w, s = make_inputs(cid)
+    xs = O.smooth_activations(x, s, wl.dtype)
+    gx = float(np.float32(448.0 / np.max(np.abs(xs))))  # a calibrated, non-power-of-two g_x
+    p = R.prepare(_g(w, wl.dtype), torch.from_numpy(s), wl.rank, 4, "mx", keep_factors=True, x_global_scale=gx)
+    y = _np(R.linear(_g(x, wl.dtype), p))
+    sel = np.arange(x.shape[0]) if rows is None else np.random.default_rng(1).choice(x.shape[0], rows, replace=False)
+    ref = O.forward_ref(x[sel], s, _np(p.left), _np(p.right), _np(p.residual), "mx", 4, wl.dtype, x_global_scale=gx)
+    err = O.rel_fro(y[sel], ref)
+    print(f"two-level workload {cid}: rel Frobenius error {err:.3e}")
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("cid,B,gx", [(5, None, 0.37), (3, 512, 1.37), (3, 100, 9.0)])
+def test_two_level_workspace_codes_bit_exact(cid, B, gx):
+    """svdq_linear's activation codes under two-level scaling are the MXFP4 codes of the
+    binary32 products RN(X^ * g_x) (white-box: the workspace begins with them)."""
+    wl = WORKLOADS[cid]
+    x, w, s = make_inputs(cid, B=B)
+    p = R.prepare(_g(w, wl.dtype), torch.from_numpy(s), wl.rank, 4, "mx", x_global_scale=gx)
+    ws = torch.full((R.workspace_bytes(x.shape[0], p),), 0xA5, dtype=torch.uint8, device=dev())
+    R.linear(_g(x, wl.dtype), p, workspace=ws)
+    torch.cuda.synchronize()
+    z = O.smooth_activations(x, s, wl.dtype).astype(np.float32) * np.float32(gx)
+    c, _ = O.quantize_mx(z)
+    want = O.pack_nibbles(c)
+    row = ((x.shape[1] + 255) // 256 * 256) // 2
+    got = ws[: x.shape[0] * row].cpu().numpy().reshape(x.shape[0], row)
+    assert np.array_equal(got[:, : want.shape[1]], want)
+    assert not got[:, want.shape[1]:].any()
+
+
+@pytest.mark.parametrize("B", [520, 16, 100])
+def test_two_level_exact_special_case(B):
+    """Rank 0, unit scale, x and W on the E2M1 grid with a 6 in every block: g_R = 2 and
+    g_x = 1/4 keep every value exact and alpha = 2, so Y = x @ W bit for bit through each
+    MXFP4 kernel."""
+    rng = np.random.default_rng(31 + B)
+    M, N = 320, 392
+    grid = O.E2M1_GRID
+    x = grid[rng.integers(0, 8, (B, M))] * np.where(rng.random((B, M)) < 0.5, -1, 1)
+    w = grid[rng.integers(0, 8, (M, N))] * np.where(rng.random((M, N)) < 0.5, -1, 1)
+    x[:, 0::32] = np.where(rng.random((B, M // 32)) < 0.5, 6.0, -4.0)
+    w[0::32, :] = np.where(rng.random((M // 32, N)) < 0.5, -6.0, 4.0)
+    p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx", x_global_scale=0.25)
+    glob = p.section(_lib.SEC_GLOBAL)[:16].cpu().numpy().view(np.float32)
+    assert glob.tolist() == [0.25, 2.0, 2.0, 0.0]
+    y = R.linear(_g(x, "bf16"), p)
+    assert np.array_equal(_bits(_np(y)), _bits(O.to_dtype(x @ w, "bf16")))

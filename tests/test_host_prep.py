@@ -229,3 +229,66 @@ def test_linear_layout_prepare_gives_the_same_blob(name, rank, fmt, bits):
     assert torch.equal(a.residual, b.residual) and (rank == 0 or torch.equal(a.left, b.left))
     with pytest.raises(ValueError):
         R.prepare(_t(w.T.copy(), dtype), torch.from_numpy(s), rank, bits, fmt, device="cpu", layout="km")
+
+
+# ----------------------------------------------------------------------------- two-level MXFP4 scaling
+def _glob(p):
+    return p.section(_lib.SEC_GLOBAL)[:16].numpy().view(np.float32)
+
+
+@pytest.mark.parametrize("name,rank,fmt,bits", [("toy", 8, "int", 4), ("bf16_small", 32, "mx", 4)])
+def test_plain_preparation_has_unit_global_scales(name, rank, fmt, bits):
+    w, s, dtype = _case(name)
+    assert _glob(_prep(w, s, dtype, rank, fmt, bits)).tolist() == [1.0, 1.0, 1.0, 0.0]
+
+
+@pytest.mark.parametrize("name,rank,gx", [("bf16_small", 32, 0.37), ("bf16_ragged", 7, 3.0), ("f32_mid", 16, 1.0),
+                                          ("toy", 0, 2.0 ** -20)])
+def test_two_level_blob_matches_oracle(name, rank, gx):
+    """Global scales, residual codes and block scales of RN(R * g_R), and the up-projection
+    factor divided by alpha, bit for bit against the oracle; L1 and the unscaled factors are
+    those of the plain preparation."""
+    w, s, dtype = _case(name)
+    M, N = w.shape
+    p = R.prepare(_t(w, dtype), torch.from_numpy(s), rank, 4, "mx", device="cpu", keep_factors=True,
+                  x_global_scale=gx)
+    plain = _prep(w, s, dtype, rank, "mx", 4)
+    res = _np(p.residual)
+    assert torch.equal(p.residual, plain.residual)
+    gr = O.two_level_residual_scale(res)
+    alpha = O.two_level_alpha(gx, gr)
+    assert _glob(p).tolist() == [np.float32(gx), gr, alpha, 0.0]
+    codes, l1t, l2t, Kp, Np, rp, _ = _sections(p)
+    c, sb = O.quantize_mx((res * gr).T)
+    want = O.pack_nibbles(c)
+    assert np.array_equal(codes[:N, : want.shape[1]], want)
+    assert not codes[N:].any() and not codes[:, want.shape[1]:].any()
+    nb = -(-M // 32)
+    tiled = p.section(_lib.SEC_RSCALES)[: Np * (Kp // 32)].numpy()
+    scales = tiled.reshape(Np // 64, Kp // 128, 64, 4).transpose(0, 2, 1, 3).reshape(Np, Kp // 32)
+    assert np.array_equal(scales[:N, :nb], sb)
+    pc, pl1t, pl2t = _sections(plain)[:3]
+    assert np.array_equal(l1t, pl1t)
+    if rank:
+        up = O.to_dtype(_np(p.right).astype(np.float64) / float(alpha), dtype)
+        if dtype == "bf16":
+            up = (up.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(l2t[:N, :rank], up.T)
+        assert torch.equal(p.right, plain.right) and torch.equal(p.left, plain.left)
+    assert not l2t[N:].any() and not l2t[:, rank:].any()
+
+
+@pytest.mark.parametrize("gx", [0.0, -1.0, float("inf"), float("nan"), 2.0 ** 65, 2.0 ** -65])
+def test_two_level_rejects_global_scales_out_of_range(gx):
+    w, s, dtype = _case("toy")
+    with pytest.raises(ValueError):
+        R.prepare(_t(w, dtype), torch.from_numpy(s), 8, 4, "mx", device="cpu", x_global_scale=gx)
+
+
+def test_two_level_needs_mx_and_the_host_split():
+    w, s, dtype = _case("toy")
+    with pytest.raises(ValueError):
+        R.prepare(_t(w, dtype), torch.from_numpy(s), 8, 4, "int", device="cpu", x_global_scale=1.0)
+    with pytest.raises(ValueError):
+        R.prepare(_t(w.T.copy(), dtype), torch.from_numpy(s), 8, 4, "mx", device="cpu", layout="nm",
+                  x_global_scale=1.0)

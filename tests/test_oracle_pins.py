@@ -438,3 +438,80 @@ def test_forward_bias_is_added_per_output_channel():
     y = O.forward_ref(x, s, left, right, res, "mx", 4, "f32")
     yb = O.forward_ref(x, s, left, right, res, "mx", 4, "f32", bias=bias)
     assert np.allclose(yb - y, bias[None, :], rtol=0, atol=1e-12 * np.abs(y).max())
+
+
+# ----------------------------------------------------------------------------- two-level MXFP4 scaling
+def test_two_level_residual_scale_worked(golden_dir):
+    from fractions import Fraction
+    with open(os.path.join(golden_dir, "two_level_worked.json")) as f:
+        g = json.load(f)
+    for case in g["residual_scale"]:
+        r = np.zeros((3, 2), np.float32)
+        r[1, 0] = -case["amax"]
+        r[2, 1] = case["amax"] / 2
+        assert O.two_level_residual_scale(r) == np.float32(float(Fraction(case["g"]))), case
+
+
+def test_two_level_residual_scale_places_the_max_at_the_top_code():
+    """g_R lies in (1, 2] and maps max|R| to 6 * 2^ex up to one rounding of the binary32
+    product, so the block holding the max takes exponent ex (or ex + 1 when that product
+    rounds just above 6 * 2^ex)."""
+    rng = _rng(41)
+    for t in range(300):
+        r = (rng.standard_normal((8, 5)) * 2.0 ** rng.integers(-60, 60)).astype(np.float32)
+        g = O.two_level_residual_scale(r)
+        assert 1.0 < g <= 2.0
+        top = np.max(np.abs(r * g))  # binary32 products
+        e = int(O.mx_block_exponent(top))
+        assert abs(float(top) / (6.0 * 2.0 ** e) - 1.0) <= 2.0 ** -22 or abs(float(top) / (6.0 * 2.0 ** (e - 1)) - 1.0) <= 2.0 ** -22
+
+
+def test_two_level_forward_worked(golden_dir):
+    with open(os.path.join(golden_dir, "two_level_worked.json")) as f:
+        g = json.load(f)["forward"]
+    x = np.zeros((1, 32), np.float32)
+    x[0, : len(g["x"])] = g["x"]
+    res = np.zeros((32, 1), np.float32)
+    res[: len(g["residual"]), 0] = g["residual"]
+    left = np.zeros((32, 1), np.float32)
+    left[1, 0] = g["left_row1"]
+    right = np.full((1, 1), g["right"], np.float32)
+    s = np.ones(32, np.float32)
+    y = O.forward_ref(x, s, left, right, res, "mx", 4, "f32")
+    assert y[0, 0] == g["y_plain"]
+    y2 = O.forward_ref(x, s, left, right, res, "mx", 4, "f32", x_global_scale=g["x_global_scale"])
+    assert abs(y2[0, 0] / g["y_two_level"] - 1.0) <= g["rel_tol_two_level"]
+    assert y2[0, 0] != y[0, 0]
+
+
+@pytest.mark.parametrize("dtype,j", [("f32", 3), ("bf16", -5), ("f32", 0)])
+def test_two_level_with_power_of_two_scales_is_plain_mx(dtype, j):
+    """When g_x = 2^j and max|R| = 3 * 2^k (so g_R = 2), every scale is a power of two: the
+    codes are those of plain MXFP4, the block exponents move by j and 1, alpha = 2^-(j+1)
+    and L2 / alpha is exact, so the two-level forward equals the plain one bit for bit."""
+    rng = _rng(7 + j)
+    x = O.to_dtype(rng.standard_t(3, (24, 100)), dtype)
+    w = O.to_dtype(0.1 * rng.standard_normal((100, 40)), dtype)
+    s = np.ones(100, np.float32)
+    left, right, res = O.split_weight(O.smooth_weight(w, s, dtype), 6, dtype)
+    res = np.array(res, np.float32)
+    k = int(np.ceil(np.log2(np.max(np.abs(res)) / 3.0))) + 1
+    res[3, 7] = 3.0 * 2.0 ** k
+    assert O.two_level_residual_scale(res) == 2.0
+    y = O.forward_ref(x, s, left, right, res, "mx", 4, dtype)
+    y2 = O.forward_ref(x, s, left, right, res, "mx", 4, dtype, x_global_scale=2.0 ** j)
+    assert np.array_equal(y, y2)
+
+
+def test_two_level_differs_from_plain_and_rejects_int():
+    """A non-power-of-two g_x changes the activation codes (the scaled values land on other
+    E2M1 points), and two-level scaling is an MXFP4-only scheme."""
+    x, w, s = make_inputs(1)
+    left, right, res = O.split_weight(O.smooth_weight(w, s, "f32"), 8, "f32")
+    y = O.forward_ref(x, s, left, right, res, "mx", 4, "f32")
+    y2 = O.forward_ref(x, s, left, right, res, "mx", 4, "f32", x_global_scale=1.37)
+    assert not np.array_equal(y, y2)
+    exact = x.astype(np.float64) @ w.astype(np.float64)
+    assert O.rel_fro(y2, exact) < 0.2 and O.rel_fro(y, exact) < 0.2
+    with pytest.raises(ValueError):
+        O.forward_ref(x, s, left, right, res, "int", 4, "f32", x_global_scale=1.0)
