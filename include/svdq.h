@@ -207,8 +207,9 @@ int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, cons
  * max|R| / 6 = f * 2^ex, f in [0.5, 1) (so g_R lies in (1, 2] and the largest |z_R| is 6 * 2^ex
  * up to rounding; g_R = 1 for an all-zero R); each call quantises the activations as
  * z_x = RN(X^ * g_x) with the caller's x_global_scale g_x (finite, in [2^-64, 2^64]; a value
- * calibrated offline, as the residual's); alpha = RN(1 / (g_x g_R)) in binary64, and the blob
- * holds D(L2^T / alpha) in SVDQ_SEC_L2T. svdq_linear then computes
+ * calibrated offline, as the residual's; every product RN(X^ * g_x) must stay finite, an
+ * overflowing one gives unspecified codes for its block); alpha = RN(1 / (g_x g_R)) in
+ * binary64, and the blob holds D(L2^T / alpha) in SVDQ_SEC_L2T. svdq_linear then computes
  * Y = D(alpha * (Q(z_x) Q(z_R) + down (L2^T / alpha)^T) [+ bias]). left_out, right_out,
  * residual_out receive the unscaled factors and R as svdq_prepare's do. fmt is SVDQ_FMT_MX,
  * bits 4. Errors as svdq_prepare, plus EINVAL for x_global_scale outside the range. */
