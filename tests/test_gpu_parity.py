@@ -584,3 +584,44 @@ def test_two_level_exact_special_case(B):
     assert glob.tolist() == [0.25, 2.0, 2.0, 0.0]
     y = R.linear(_g(x, "bf16"), p)
     assert np.array_equal(_bits(_np(y)), _bits(O.to_dtype(x @ w, "bf16")))
+
+
+# ----------------------------------------------------------------------------- seeded shape sweep
+def _sweep_cases(n=24, seed=2026):
+    """Ragged shapes drawn from a fixed seed: B in [1, 600] (every kernel route), M in [1, 2600]
+    (short and multi-stage K, partial 32-blocks), N in [1, 700], rank in [0, min(M, N, 80)],
+    both formats, INT widths 2-8, both dtypes, and a bias on every third case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        fmt = "mx" if c % 2 else "int"
+        dtype = "f32" if c % 5 == 0 else "bf16"
+        bits = 4 if fmt == "mx" else int(rng.integers(2, 9))
+        B = int(rng.choice([1, 3, 16, 17, 40, 64, 65, 130, 255, 256, 300, 600]))
+        M = int(rng.integers(1, 2601))
+        N = int(rng.integers(1, 701))
+        rank = int(rng.integers(0, min(M, N, 80) + 1))
+        out.append((c, B, M, N, rank, fmt, bits, dtype, c % 3 == 0))
+    return out
+
+
+@pytest.mark.parametrize("c,B,M,N,rank,fmt,bits,dtype,bias", _sweep_cases())
+def test_parity_shape_sweep(c, B, M, N, rank, fmt, bits, dtype, bias):
+    rng = np.random.default_rng(1000 + c)
+    x = O.to_dtype(rng.standard_t(3, (B, M)), dtype)
+    w = O.to_dtype(0.05 * rng.standard_normal((M, N)) + 0.1 * rng.standard_normal((M, 2)) @ rng.standard_normal((2, N)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.5)
+    b = O.to_dtype(rng.standard_normal(N), dtype) if bias else None
+    print(f"case {c}: B={B} M={M} N={N} rank={rank} {fmt}{bits} {dtype} bias={bias}", flush=True)
+    p = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, bits, fmt, keep_factors=True)
+    xg = _g(x, dtype)
+    bg = None if b is None else _g(b, dtype)
+    y = R.linear(xg, p, bias=bg)
+    y2 = R.linear(xg, p, bias=bg)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), fmt, bits, dtype, bias=b)
+    err = O.rel_fro(_np(y), ref)
+    print(f"case {c}: rel Frobenius error {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
