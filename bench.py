@@ -40,7 +40,8 @@ def gemm_kernel(wl, B):
         return "k_gemm_decode_mx", os.path.join(CSRC, "k_gemm_decode.hip")
     if wl.fmt == "mx" and wl.dtype == "bf16" and B >= 256:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
-    if wl.fmt == "int" and wl.bits <= 4:
+    kp = -(-wl.M // 256) * 256
+    if wl.fmt == "int" and wl.bits <= 4 and kp // 256 >= 6:  # the INT4 kernel keeps 6 stages of 256 codes in flight
         return "k_gemm_int4", os.path.join(CSRC, "k_gemm_int.hip")
     return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0;
 
-  // Pipeline (DIST = 2 stages in flight, NS = DIST + 2 buffers): stage s+DIST is issued at
+  // Pipeline (DIST stages in flight, NS = DIST + 2 buffers): stage s+DIST is issued at
   // the top of iteration s; the first 16-code half of stage s is unpacked and fed to the
   // matrix cores; then the wave waits for its own loads of stage s+1, one barrier publishes
   // every wave's loads of that stage, and its operands are read from LDS while the second
