@@ -241,6 +241,154 @@ def test_mx_exact_special_case(dtype):
     assert np.array_equal(_bits(_np(y)), _bits(want))
 
 
+# ----------------------------------------------------------------------------- exact cases per GEMM kernel
+def _gemm_route(B, M, N, fmt, bits, dtype):
+    """The residual GEMM kernel (and MXFP4 tile) svdq_linear launches for a shape: the launch
+    rules of the library, restated so that each exact case below names the kernel it aims at."""
+    kp = -(-M // 256) * 256
+    if fmt == "mx" and dtype == "bf16" and B <= 64:
+        return "decode"
+    if fmt == "mx" and dtype == "bf16" and B >= 256:
+        tiles_m = -(-B // 256)
+        if N % 256 == 0 and tiles_m * (N // 256) >= 512:
+            return "mx256x256"
+        return "mx256x192" if N % 192 == 0 else "mx256x256"
+    if fmt == "int" and bits <= 4 and kp // 256 >= 6:
+        return "int4"
+    return "generic"
+
+
+def _e2m1_exact_operands(rng, B, M, N):
+    """x [B, M] and W [M, N] on the E2M1 grid with every 32-block (rows of x, columns of W)
+    holding a 4 or a 6 as its largest magnitude: the shared exponents are 0 and quantisation
+    is the identity, so with rank 0 and unit scale Y = x @ W, a sum of multiples of 1/4 below
+    2^24 / 4 in magnitude, exact in float32 and rounded once to bf16."""
+    grid = O.E2M1_GRID
+    x = grid[rng.integers(0, 8, (B, M))] * np.where(rng.random((B, M)) < 0.5, -1, 1)
+    w = grid[rng.integers(0, 8, (M, N))] * np.where(rng.random((M, N)) < 0.5, -1, 1)
+    x[:, 0::32] = np.where(rng.random((B, -(-M // 32))) < 0.5, 6.0, -4.0)
+    w[0::32, :] = np.where(rng.random((-(-M // 32), N)) < 0.5, -6.0, 4.0)
+    return x, w
+
+
+@pytest.mark.parametrize("B,M,N,bits,dtype", [
+    (256, 4096, 4096, 4, "bf16"),   # the INT4 workload's shape: 64 x 64 tiles, 16 K stages
+    (130, 1792, 200, 3, "f32"),     # 7 stages (one odd steady iteration), ragged B and N, float32 io
+    (70, 1536, 328, 2, "bf16"),     # exactly the 6 stages kept in flight, ragged N tile
+])
+def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
+    """Rank 0, unit scale, integer x and W with max |.| = qmax through the INT4 kernel (K of at
+    least six 256-code stages): s_x = s_R = 1 and Y = x @ W bit for bit. |Y| <= qmax^2 K < 2^24,
+    so the float32 result is exact and the bf16 one is its single rounding."""
+    assert _gemm_route(B, M, N, "int", bits, dtype) == "int4"
+    rng = np.random.default_rng(B + M + bits)
+    q = 2 ** (bits - 1) - 1
+    x = rng.integers(-q, q + 1, (B, M)).astype(np.float32)
+    w = rng.integers(-q, q + 1, (M, N)).astype(np.float32)
+    x[0, 0] = w[0, 0] = q
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, bits, "int")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x.astype(np.float64) @ w.astype(np.float64), dtype)
+    got = _np(y)
+    bad = np.argwhere(_bits(got) != _bits(want))
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("B,M,N,route", [
+    (520, 512, 576, "mx256x192"),    # the attention-projection tile (N a multiple of 192), ragged B
+    (4096, 256, 8192, "mx256x256"),  # 512 tiles of 256 x 256: the MLP up-projection's tile choice
+    (16, 1024, 392, "decode"),       # decode kernel, one 16-row tile, eight waves
+    (17, 1280, 200, "decode"),       # decode kernel, two row tiles (the second with one live row)
+    (40, 768, 96, "decode"),         # decode kernel, four row tiles and four waves
+])
+def test_mx_kernel_exact_special_case(B, M, N, route):
+    """Plain (not two-level) MXFP4 exact case through each MXFP4 kernel and tile choice."""
+    assert _gemm_route(B, M, N, "mx", 4, "bf16") == route
+    x, w = _e2m1_exact_operands(np.random.default_rng(B + N), B, M, N)
+    p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx")
+    y = R.linear(_g(x, "bf16"), p)
+    want = O.to_dtype(x @ w, "bf16")
+    got = _np(y)
+    bad = np.argwhere(_bits(got) != _bits(want))
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
+# ----------------------------------------------------------------------------- the hardware E2M1 conversion
+def _sweep_blocks(dtype, values_for):
+    """Activation rows for a sweep of the E2M1 coding: for every shared exponent e from -127 to
+    126, blocks of 32 whose element 0 is the block maximum (6 * 2^e, or the dtype's largest
+    finite value where 6 * 2^e is beyond it; sign alternating) and whose other 31 elements are
+    the values under test (values_for(e), all at most that maximum in magnitude). Rows hold 256
+    blocks (K = 8192); the last row is padded with zero blocks."""
+    fmax = {"bf16": float(np.uint32(0x7F7F0000).view(np.float32)), "f32": float(np.finfo(np.float32).max)}[dtype]
+    blocks = []
+    for e in range(-127, 127):
+        cap = min(6.0 * 2.0 ** e, fmax)
+        v = values_for(e, cap)
+        assert np.all(np.abs(v.astype(np.float64)) <= cap)
+        nb = -(-len(v) // 31)
+        body = np.zeros(nb * 31, np.float32)
+        body[: len(v)] = v
+        blk = np.empty((nb, 32), np.float32)
+        blk[:, 1:] = body.reshape(nb, 31)
+        blk[:, 0] = np.where(np.arange(nb) % 2 == 0, cap, -cap)
+        blocks.append(blk)
+    allb = np.concatenate(blocks)
+    rows = -(-len(allb) // 256)
+    out = np.zeros((rows * 256, 32), np.float32)
+    out[: len(allb)] = allb
+    return out.reshape(rows, 256 * 32)
+
+
+def _check_codes_chunked(x, dtype):
+    s = np.ones(x.shape[1], np.float32)
+    codes, scales, _ = R.quantize_activations(_g(x, dtype), torch.from_numpy(s).to(dev()), "mx", 4)
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    for r0 in range(0, x.shape[0], 64):
+        c, sb = O.quantize_mx(x[r0:r0 + 64].astype(np.float64))
+        wc = O.pack_nibbles(c)
+        gc = codes[r0:r0 + 64, : wc.shape[1]]
+        bad = np.argwhere(gc != wc)
+        assert bad.size == 0, f"codes differ at row {r0 + bad[0][0]}, byte {bad[0][1]}"
+        assert np.array_equal(scales[r0:r0 + 64, : sb.shape[1]], sb), f"E8M0 bytes differ in rows {r0}.."
+
+
+def test_e2m1_conversion_every_bf16_value():
+    """Every finite bf16 value of either sign, against every shared exponent e in [-127, 126]
+    whose block maximum 6 * 2^e it does not exceed (subnormal values, subnormal 2^-127 block
+    scales, every tie and every E2M1 boundary included): codes and E8M0 bytes bit-equal to the
+    oracle's quantize_mx."""
+    mags = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+
+    def values_for(e, cap):
+        v = mags[mags.astype(np.float64) <= cap]
+        return np.concatenate([v, -v])
+
+    _check_codes_chunked(_sweep_blocks("bf16", values_for), "bf16")
+
+
+def test_e2m1_conversion_dense_f32():
+    """float32 activations: for every shared exponent, 1024 significands per binade over the
+    whole coded range [2^-4, 6] * 2^e, every E2M1 rounding midpoint and its neighbours within 2
+    ulps, and values far below the smallest code, both signs; the values are RN_f32(m * 2^e), so
+    at the bottom of the range they are float32 subnormals."""
+    rng = np.random.default_rng(5)
+    sig = np.concatenate([np.ldexp(1.0 + np.arange(1024) / 1024.0, k) for k in range(-4, 3)])
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 8),
+                           np.nextafter(np.nextafter(mids, 0), 0), np.nextafter(np.nextafter(mids, 8), 8)])
+    ms = np.concatenate([sig[sig <= 6.0], near.astype(np.float64), [4.0, 6.0, 0.0, 1e-3, 3e-9],
+                         rng.random(64) * 6.0])
+
+    def values_for(e, cap):
+        v = (ms * 2.0 ** e).astype(np.float32)
+        v = v[np.abs(v.astype(np.float64)) <= cap]
+        return np.concatenate([v, -v])
+
+    _check_codes_chunked(_sweep_blocks("f32", values_for), "f32")
+
+
 # ----------------------------------------------------------------------------- the operator
 def _parity(cid, B=None, rank=None, rows=None):
     wl = WORKLOADS[cid]
@@ -273,8 +421,9 @@ def test_operator_parity_full_size(cid):
 
 
 @pytest.mark.parametrize("cid", [3, 4])
-def test_operator_parity_full_size_sampled_rows(cid):
-    _parity(cid, rows=256)
+def test_operator_parity_full_size_every_row(cid):
+    """The two large MXFP4 workloads (4096 rows) against the oracle on every output."""
+    _parity(cid)
 
 
 @pytest.mark.parametrize("cid,B", [(3, 77), (4, 130), (2, 33)])

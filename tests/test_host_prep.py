@@ -292,3 +292,29 @@ def test_two_level_needs_mx_and_the_host_split():
     with pytest.raises(ValueError):
         R.prepare(_t(w.T.copy(), dtype), torch.from_numpy(s), 8, 4, "mx", device="cpu", layout="nm",
                   x_global_scale=1.0)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_split_eckart_young_at_workload_shapes(cid):
+    """The library's truncated SVD at the shapes it serves (4096 x 4096 rank 32, 3072 x 3072
+    rank 32, 3072 x 12288 rank 32, 8192 x 8192 rank 128: all on the randomized subspace
+    route): ||R||_F of svdq_prepare's residual within 1e-3 of the exact tail
+    sqrt(sum_{i>r} sigma_i^2) of the smoothed weight. The tail comes from an independent route:
+    ||ws||_F^2 minus the r largest eigenvalues of the float64 Gram matrix (LAPACK's symmetric
+    eigensolver), no SVD. At 8192 x 8192 the rank (128) cuts into the noise bulk, where
+    consecutive singular values are closest."""
+    import scipy.linalg
+
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[cid]
+    _, w, s = make_inputs(cid, B=64)
+    p = R.prepare(torch.from_numpy(w).to(TD[wl.dtype]), torch.from_numpy(s), wl.rank, wl.bits, wl.fmt, device="cpu",
+                  keep_factors=True)
+    ws = O.smooth_weight(w, s, wl.dtype).astype(np.float64)
+    gram = ws @ ws.T if ws.shape[0] <= ws.shape[1] else ws.T @ ws
+    n = gram.shape[0]
+    top = scipy.linalg.eigh(gram, eigvals_only=True, subset_by_index=[n - wl.rank, n - 1])
+    tail = np.sqrt(np.sum(ws * ws) - top.sum())
+    res = np.linalg.norm(_np(p.residual).astype(np.float64))
+    assert abs(res - tail) <= 1e-3 * tail, (res, tail)
