@@ -10,7 +10,8 @@ Prints one JSON line: value = 2*B*M*N*steps / wall time (TFLOP/s, eager launches
 the roofline of the dominant kernel (the residual GEMM, timed with HIP events the library
 records around its own launches), and the CPU oracle's throughput on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]   (default workload 4,
+       MXFP4 4096 x 3072 x 12288, the largest single-GPU configuration)
        python bench.py --pmc-summary FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES
        python bench.py --workload W --mfma-summary COUNTERS.csv
 """
@@ -46,8 +47,18 @@ def gemm_kernel(wl, B):
     return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 
 
+def sampling_stride(steps):
+    """Every how many timed calls the residual GEMM's dispatch carries an event pair: at least
+    16 sampled launches whatever the step count."""
+    return max(1, steps // 16)
+
+
 def algorithmic(wl, B):
-    """Algorithmic work of one call and of one launch of the residual GEMM kernel."""
+    """Algorithmic work of one call and of one launch of the residual GEMM kernel.
+
+    call_bytes: what one call must move (x, scale, Y, packed residual codes and E8M0 scales,
+    both low-rank factors); gemm_bytes: the operands and output of the residual GEMM alone
+    (activation codes and scales, residual codes and scales, down, L2, Y)."""
     e = 2 if wl.dtype == "bf16" else 4
     M, N, r = wl.M, wl.N, wl.rank
     mx = wl.fmt == "mx"
@@ -57,6 +68,35 @@ def algorithmic(wl, B):
     call = B * M * e + 4 * M + B * N * e + code_bytes(N, M) + r_scales + (M + N) * r * e
     gemm = code_bytes(B, M) + a_scales + code_bytes(N, M) + r_scales + B * r * e + N * r * e + B * N * e
     return {"flops": 2.0 * B * M * N, "call_bytes": call, "gemm_bytes": gemm}
+
+
+def roofline(wl, B, work, gemm_ms, call_ms):
+    """Roofline of the residual GEMM kernel (flops and its own operand bytes over its average
+    launch duration) with both fractions; `bound` is whichever peak time is larger. `call`
+    gives the same two fractions for a whole svdq_linear call: 2BMN and the call's
+    algorithmic bytes (x, scale, Y, residual codes and scales, L1, L2) over the eager time per
+    call."""
+    mfma_peak = PEAK["mxfp4"] if wl.fmt == "mx" else PEAK["int8"]
+    gemm_s, call_s = gemm_ms / 1e3, call_ms / 1e3
+    t_mfma = work["flops"] / (mfma_peak * 1e12)
+    t_hbm = work["gemm_bytes"] / (PEAK["hbm"] * 1e9)
+    tf = work["flops"] / gemm_s / 1e12
+    gb = work["gemm_bytes"] / gemm_s / 1e9
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": tf, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tf / mfma_peak}
+    else:
+        roof = {"bound": "hbm", "achieved": gb, "peak": PEAK["hbm"], "unit": "GB/s", "frac": gb / PEAK["hbm"]}
+    roof.update({
+        "traffic": None, "kernel": gemm_kernel(wl, B)[0], "avg_ms": gemm_ms,
+        "algorithmic_bytes": work["gemm_bytes"], "frac_mfma": tf / mfma_peak, "frac_hbm": gb / PEAK["hbm"],
+        "call": {"bound": "mfma" if work["flops"] / (mfma_peak * 1e12) >= work["call_bytes"] / (PEAK["hbm"] * 1e9)
+                 else "hbm",
+                 "us": call_ms * 1e3, "tflops": work["flops"] / call_s / 1e12,
+                 "frac_mfma": work["flops"] / call_s / 1e12 / mfma_peak,
+                 "algorithmic_bytes": work["call_bytes"], "gbs": work["call_bytes"] / call_s / 1e9,
+                 "frac_hbm": work["call_bytes"] / call_s / 1e9 / PEAK["hbm"]},
+    })
+    return roof
 
 
 def source_sha(path):
@@ -191,11 +231,11 @@ def run(args):
 
     # ---- timed region: eager launches. The library passes one HIP event pair to the
     # residual-GEMM dispatch of every EVERY-th call (stage 3 only): the roofline's kernel
-    # duration comes from the timed calls themselves, while an event pair on every call
-    # (about 10 us of host time each) would make the loop host-bound. EVERY is 16, or down to
-    # 8 for short runs, so that the average rests on a few dozen launches.
+    # duration comes from the timed calls themselves. EVERY = steps // 16 (at least 1), so the
+    # average always rests on at least 16 launches (every launch of a short run) while long
+    # runs of short calls do not become host-bound on the event records.
     GEMM_STAGE = 3
-    EVERY = max(8, min(16, args.steps // 50))
+    EVERY = sampling_stride(args.steps)
     L.check(lib.svdq_profile_begin_sampled(max(1, args.steps // EVERY + 1), 1 << GEMM_STAGE, EVERY))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -250,24 +290,11 @@ def run(args):
         graph = {"ms_per_step": t_graph / (reps * per_graph) * 1e3,
                  "value": work["flops"] * reps * per_graph / t_graph / 1e12, "calls_per_graph": per_graph}
 
-    # ---- roofline of the dominant kernel (the residual GEMM)
-    gemm_s = gemm_ms / 1e3
-    mfma_peak = PEAK["mxfp4"] if wl.fmt == "mx" else PEAK["int8"]
-    t_mfma = work["flops"] / (mfma_peak * 1e12)
-    t_hbm = work["gemm_bytes"] / (PEAK["hbm"] * 1e9)
-    traffic = pmc_traffic(wl, B)
-    if t_mfma >= t_hbm:
-        ach = work["flops"] / gemm_s / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak}
-    else:
-        ach = work["gemm_bytes"] / gemm_s / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]}
-    roof["traffic"] = traffic
+    # ---- roofline of the dominant kernel (the residual GEMM), and of the whole call
+    roof = roofline(wl, B, work, gemm_ms, t_eager / args.steps * 1e3)
+    roof["traffic"] = pmc_traffic(wl, B)
     if roof["bound"] == "mfma":
         roof["mfma_util"] = pmc_mfma_util(wl, B)  # counter evidence: MFMA busy / active cycles
-    roof["kernel"] = gemm_kernel(wl, B)[0]
-    roof["avg_ms"] = gemm_ms
-    roof["algorithmic_bytes"] = work["gemm_bytes"]
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -498,9 +525,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=800)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="1 toy f32 INT4, 2 INT4 W4A4 bf16 (default), 3 MXFP4 DiT attention, 4 MXFP4 MLP up, "
-                         "5 MXFP4 decode")
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="1 toy f32 INT4, 2 INT4 W4A4 bf16, 3 MXFP4 DiT attention, 4 MXFP4 MLP up (default: the "
+                         "largest single-GPU workload), 5 MXFP4 decode")
     ap.add_argument("--rotate-mb", type=float, default=512.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")

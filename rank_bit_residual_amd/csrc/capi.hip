@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <string>
-#include <vector>
+#include <type_traits>
 
 #include "launch.h"
 #include "svdq_internal.h"
@@ -56,16 +56,19 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
-// Kernel-timing session (svdq_profile_begin / svdq_profile_end).
+// Kernel-timing session (svdq_profile_begin / svdq_profile_end). Plain data with no
+// destructor: the arrays are released by svdq_profile_end, so nothing of this state runs at
+// process exit, when the HIP runtime (or a profiler attached to it) may already be gone.
 struct Profile {
-  bool open = false;
-  int max_calls = 0, calls = 0;  // recorded calls: capacity and count
-  int every = 1, seen = 0;        // record calls seen % every == 0
-  unsigned mask = 0;              // stages that record events
-  std::vector<hipEvent_t> ev;     // [call][stage][begin, end]
-  std::vector<uint8_t> recorded;  // [call][stage]: both events of the pair were recorded
+  bool open;
+  int max_calls, calls;  // recorded calls: capacity and count
+  int every, seen;       // record calls seen % every == 0
+  unsigned mask;         // stages that record events
+  hipEvent_t* ev;        // [call][stage][begin, end], max_calls * SVDQ_NSTAGES * 2 (new[])
+  uint8_t* recorded;     // [call][stage]: both events of the pair were recorded (new[])
 };
-Profile g_prof;
+Profile g_prof;  // zero-initialised: no session open
+static_assert(std::is_trivially_destructible<Profile>::value, "no exit-time destructor");
 }  // namespace
 
 thread_local GemmEvents g_gemm_events;
@@ -395,17 +398,18 @@ int svdq_profile_begin_sampled(int max_calls, unsigned stage_mask, int every) {
   if (every < 1) return set_error(SVDQ_EINVAL, "every must be >= 1");
   if (stage_mask == 0 || (stage_mask >> SVDQ_NSTAGES)) return set_error(SVDQ_EINVAL, "stage_mask must select stages 0..3");
   if (g_prof.open) return set_error(SVDQ_EINVAL, "a profiling session is already open");
-  g_prof.ev.assign((size_t)max_calls * SVDQ_NSTAGES * 2, nullptr);
-  for (auto& e : g_prof.ev) {
-    hipError_t r = hipEventCreate(&e);
+  const size_t nev = (size_t)max_calls * SVDQ_NSTAGES * 2;
+  g_prof.ev = new hipEvent_t[nev]();
+  for (size_t i = 0; i < nev; i++) {
+    hipError_t r = hipEventCreate(&g_prof.ev[i]);
     if (r != hipSuccess) {
-      for (auto& f : g_prof.ev)
-        if (f) hipEventDestroy(f);
-      g_prof.ev.clear();
+      for (size_t j = 0; j < i; j++) hipEventDestroy(g_prof.ev[j]);
+      delete[] g_prof.ev;
+      g_prof.ev = nullptr;
       return hip_status(r, "hipEventCreate");
     }
   }
-  g_prof.recorded.assign((size_t)max_calls * SVDQ_NSTAGES, 0);
+  g_prof.recorded = new uint8_t[(size_t)max_calls * SVDQ_NSTAGES]();
   g_prof.open = true;
   g_prof.mask = stage_mask;
   g_prof.max_calls = max_calls;
@@ -431,9 +435,12 @@ int svdq_profile_end(float* ms, int cap, int* n_calls) {
       if (ms) ms[(size_t)c * SVDQ_NSTAGES + k] = v;
     }
   }
-  for (auto& e : g_prof.ev) hipEventDestroy(e);
-  g_prof.ev.clear();
-  g_prof.recorded.clear();
+  const size_t nev = (size_t)g_prof.max_calls * SVDQ_NSTAGES * 2;
+  for (size_t i = 0; i < nev; i++) hipEventDestroy(g_prof.ev[i]);
+  delete[] g_prof.ev;
+  delete[] g_prof.recorded;
+  g_prof.ev = nullptr;
+  g_prof.recorded = nullptr;
   g_prof.open = false;
   clear_stale_hip_error();
   if (n_calls) *n_calls = n;

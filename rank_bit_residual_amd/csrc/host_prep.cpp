@@ -27,14 +27,20 @@
 namespace svdq {
 
 namespace {
-thread_local std::string g_last_error;
-}
+// A fixed buffer rather than a std::string: thread-local storage with no destructor, so
+// nothing of the library runs at thread or process exit (after the HIP runtime or a
+// profiler attached to it may already have shut down).
+constexpr size_t kErrLen = 512;
+thread_local char g_last_error[kErrLen];
+}  // namespace
 
 int set_error(int status, const std::string& msg) {
-  g_last_error = msg;
+  const size_t n = std::min(msg.size(), kErrLen - 1);
+  std::memcpy(g_last_error, msg.data(), n);
+  g_last_error[n] = '\0';
   return status;
 }
-void clear_error() { g_last_error.clear(); }
+void clear_error() { g_last_error[0] = '\0'; }
 
 int check_dtype(int dtype) {
   if (dtype == SVDQ_F32 || dtype == SVDQ_BF16) return SVDQ_OK;
@@ -214,7 +220,7 @@ using namespace svdq;
 
 extern "C" {
 
-const char* svdq_last_error(void) { return g_last_error.c_str(); }
+const char* svdq_last_error(void) { return g_last_error; }
 
 const char* svdq_version(void) { return "svdq 0.1 gfx950"; }
 

@@ -52,3 +52,52 @@ def test_refusals_exit_before_touching_a_gpu(argv, monkeypatch, capsys):
     assert bench.main() == 2
     err = capsys.readouterr().err
     assert ("one GPU only" in err) if argv[0] == "--gpus" else ("--steps" in err)
+
+
+def test_call_bytes_mlp_up():
+    """The whole call's algorithmic bytes at the MXFP4 MLP up-projection workload (B 4096,
+    M 3072, N 12288, rank 32, bf16): what the method must move, intermediates excluded."""
+    wl = WORKLOADS[4]
+    parts = {
+        "x": 4096 * 3072 * 2,
+        "scale": 3072 * 4,
+        "Y": 4096 * 12288 * 2,
+        "residual codes": 3072 * 12288 // 2,
+        "residual E8M0": 3072 * 12288 // 32,
+        "L1 + L2": (3072 + 12288) * 32 * 2,
+    }
+    assert bench.algorithmic(wl, wl.B)["call_bytes"] == sum(parts.values()) == 146878464
+
+
+@pytest.mark.parametrize("steps", [1, 5, 16, 20, 31, 800, 5000])
+def test_gemm_sampling_keeps_16_launches(steps):
+    """The sampled GEMM timing records every launch of a short run and at least 16 launches of
+    any run."""
+    every = bench.sampling_stride(steps)
+    sampled = len(range(0, steps, every))
+    assert sampled >= min(16, steps)
+
+
+def test_roofline_fractions():
+    """Both fractions of the GEMM kernel and of the whole call, from hand-computed times."""
+    wl = WORKLOADS[4]
+    w = bench.algorithmic(wl, wl.B)
+    r = bench.roofline(wl, wl.B, w, gemm_ms=0.1, call_ms=0.125)
+    assert r["bound"] == "mfma" and r["kernel"] == "k_gemm_mx"
+    assert r["frac"] == pytest.approx(w["flops"] / 1e-4 / 1e12 / 10100.0)
+    assert r["frac_hbm"] == pytest.approx(w["gemm_bytes"] / 1e-4 / 1e9 / 8000.0)
+    assert r["call"]["frac_mfma"] == pytest.approx(w["flops"] / 1.25e-4 / 1e12 / 10100.0)
+    assert r["call"]["frac_hbm"] == pytest.approx(w["call_bytes"] / 1.25e-4 / 1e9 / 8000.0)
+    d = WORKLOADS[5]
+    assert bench.roofline(d, d.B, bench.algorithmic(d, d.B), 0.01, 0.015)["bound"] == "hbm"
+
+
+def test_default_workload_is_the_largest(monkeypatch):
+    """With no --workload the bench runs the MXFP4 MLP up-projection (4096 x 3072 x 12288), the
+    largest configuration that fits one GPU."""
+    seen = {}
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    monkeypatch.setattr(bench, "run", lambda args: seen.setdefault("w", args.workload))
+    assert bench.main() == 0 and seen["w"] == 4
+    flops = {c: WORKLOADS[c].B * WORKLOADS[c].M * WORKLOADS[c].N for c in WORKLOADS}
+    assert max(flops, key=flops.get) == 4
