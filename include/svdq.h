@@ -264,6 +264,30 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
                      svdq_stream_t stream);
 
 /* --------------------------------------------------------------------------------------
+ * svdq_linear_noalloc — svdq_linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * kernels and results as svdq_linear with no bias (bit for bit), but the workspace is the
+ * library's own: a device array of SVDQ_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from
+ * the moment the library is loaded on that GPU until the process ends. The call allocates
+ * and frees nothing (no hipMalloc/hipFree, no allocating library routine); the caller still
+ * passes x, the prepared blob and y. The scratch needs no clearing: every byte a call reads
+ * there was written earlier in the same call.
+ *   Arguments as svdq_linear without the workspace. `stream` must belong to the current
+ *   device (whose scratch the call uses); its address is looked up on the first call on each
+ *   device (hipGetSymbolAddress).
+ *   Calls on one GPU share its scratch: calls that may overlap in time on one GPU (different
+ *   streams, or different host threads without ordering) race and give undefined results;
+ *   calls ordered on one stream are safe.
+ * Errors: as svdq_linear; EINVAL when the shape's workspace (svdq_workspace_bytes) exceeds
+ *   SVDQ_NOALLOC_SCRATCH_BYTES (e.g. MXFP4 bf16 with B * M above ~24 M elements) or the
+ *   stream belongs to another device; EUNSUPPORTED for device indices above 63.
+ * ------------------------------------------------------------------------------------ */
+#define SVDQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int svdq_linear_noalloc(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob,
+                        int64_t N, int64_t rank, int fmt, int bits, int dtype,
+                        void* y, int64_t ldy, svdq_stream_t stream);
+
+/* --------------------------------------------------------------------------------------
  * svdq_quantize_activations — step (a) alone, for bit-exact checks ([EX] "Formula and
  * conventions" item 3 for INT; [MS] step 2 for MX). Device call.
  *   x [B,M] dtype row stride ldx; scale [M] f32 device.

@@ -30,6 +30,8 @@ SIGNATURES = {
                             c_sz, c_vp]),
     "svdq_linear_bias": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp,
                                  c_i64, c_vp, c_sz, c_vp]),
+    "svdq_linear_noalloc": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_i64,
+                                    c_vp]),
     "svdq_quantize_activations": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp,
                                           c_i64, c_vp, c_vp, c_sz, c_vp]),
     "svdq_prepare_gpu_workspace_bytes": (c_int, [c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]),
@@ -53,6 +55,7 @@ SVDQ_F32, SVDQ_BF16, SVDQ_F64 = 0, 1, 2
 SVDQ_FMT_INT, SVDQ_FMT_MX = 0, 1
 SEC_SCALE, SEC_RCODES, SEC_RSCALES, SEC_L1T, SEC_L2T, SEC_RECIP, SEC_GLOBAL, SEC_END = 0, 1, 2, 3, 4, 5, 6, 7
 NSEC = 8
+NOALLOC_SCRATCH_BYTES = 16 << 20  # SVDQ_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 

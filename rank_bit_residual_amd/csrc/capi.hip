@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <string>
 #include <type_traits>
@@ -388,6 +389,65 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   tm.gemm_end(ge);
   st = hip_status(ge, "residual GEMM launch");
   return st;
+}
+
+// ---- svdq_linear_noalloc: svdq_linear with a library-owned scratch instead of a workspace.
+// The scratch is one file-scope device array per GPU (each device holds its own copy from the
+// moment the library's code object is loaded until the process ends). In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address is looked up once
+// per device with hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[SVDQ_NOALLOC_SCRATCH_BYTES];
+
+namespace svdq {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // per-device address of `scratch`, or null
+
+// Device address of this device's scratch (the current device, which the stream must belong
+// to); looked up on the first call on each device. Concurrent first calls look it up twice
+// and store the same address.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return set_error(SVDQ_EUNSUPPORTED, "device index above 63");
+  hipDevice_t sdev = -1;
+  if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+  if ((int)sdev != dev) return set_error(SVDQ_EINVAL, "the stream belongs to another device than the current one");
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    if ((e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch))) != hipSuccess) return hip_status(e, "hipGetSymbolAddress");
+    if (!a || !aligned(a, kAlign)) return set_error(SVDQ_EHIP, "scratch symbol has no aligned device address");
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *out = a;
+  return SVDQ_OK;
+}
+}  // namespace
+}  // namespace svdq
+
+extern "C" {
+
+int svdq_linear_noalloc(const void* x, int64_t B, int64_t M, int64_t ldx, const void* blob, int64_t N, int64_t rank,
+                        int fmt, int bits, int dtype, void* y, int64_t ldy, svdq_stream_t stream) {
+  clear_error();
+  int st = check_linear_dims(B, M, N, rank, fmt, bits, dtype);
+  if (st) return st;
+  const Dims d = make_dims(M, N, rank, fmt, bits, dtype);
+  int64_t woff[WS_NSEC];
+  workspace_layout(d, make_plan(d, B), woff);
+  if (woff[WS_END] > (int64_t)SVDQ_NOALLOC_SCRATCH_BYTES)
+    return set_error(SVDQ_EINVAL, "svdq_linear_noalloc: this shape needs " + std::to_string(woff[WS_END]) +
+                                      " bytes of scratch, above its maximum of " +
+                                      std::to_string((int64_t)SVDQ_NOALLOC_SCRATCH_BYTES) +
+                                      " (use svdq_linear with a caller workspace)");
+  void* ws = nullptr;
+  if ((st = scratch_address((hipStream_t)stream, &ws))) return st;
+  return svdq_linear_bias(x, B, M, ldx, blob, N, rank, fmt, bits, dtype, nullptr, y, ldy, ws,
+                          (size_t)SVDQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int svdq_profile_begin(int max_calls, unsigned stage_mask) { return svdq_profile_begin_sampled(max_calls, stage_mask, 1); }
