@@ -18,8 +18,9 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   LaunchPlan p;
   p.B = B;
   p.row_blocks = (int)ceil_div(B, 16);
-  // 16-wide rank chunks when 64-wide ones would leave most of the chip idle (decode batches)
-  p.rchunk = (d.rp > 0 && (int64_t)p.row_blocks * ceil_div(d.rp, 64) < 256) ? 16 : 64;
+  // 16-wide rank chunks when 64-wide ones would leave most of the chip idle (decode batches);
+  // otherwise one 32-wide chunk for ranks up to 32 (its operands travel a step ahead), else 64
+  p.rchunk = (d.rp > 0 && (int64_t)p.row_blocks * ceil_div(d.rp, 64) < 256) ? 16 : (d.rp <= 32 ? 32 : 64);
   p.r_chunks = d.rp > 0 ? (int)ceil_div(d.rp, p.rchunk) : 1;
   // Split K across blocks only when rows x low-rank chunks give fewer than ~256 blocks, and
   // never below one 128-wide step per wave of a block (8 waves: 1024 K per chunk).

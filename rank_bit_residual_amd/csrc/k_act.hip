@@ -281,10 +281,30 @@ __device__ __forceinline__ void load_l1(const ActParams& p, const ActLane& L, in
     }
 }
 
-// Whether a full step's L1^T operands travel one step ahead with its x: with 16 rank columns
-// per block (16 registers); the 64-wide form would run out of registers, so it loads them at
-// the start of the step.
-constexpr bool l1_ahead(int RC) { return RC == 16; }
+// The same for the full steps of a block with low-rank columns (nbl >= 1), with a fixed number
+// of loads: tiles past the block's last (only in a partial 64-wide chunk) reload that one, their
+// operands unused. The compiler counts the loads issued after an operand to wait for it alone;
+// a conditional load would make that count unknown and the wait cover every later load, the
+// next step's prefetch included.
+template <int RC, class T>
+__device__ __forceinline__ void load_l1_all(const ActParams& p, const ActLane& L, int k0, v4i (&bw)[RC / 16][4]) {
+  const T* __restrict__ l1t = reinterpret_cast<const T*>(p.l1t);
+#pragma unroll
+  for (int n = 0; n < RC / 16; n++) {
+    const int tn = n < L.nbl ? n : L.nbl - 1;
+    const T* tile = l1t + ((int64_t)(L.rbase / 16 + tn) * (p.Kp / 128) + k0 / 128) * 2048 + L.lane * (16 / sizeof(T));
+#pragma unroll
+    for (int c = 0; c < 4; c++) bw[n][c] = *reinterpret_cast<const v4i*>(tile + c * 512);
+  }
+}
+
+// Whether a full step's L1^T operands travel one step ahead with its x: with 16 or 32 rank
+// columns per block (16 or 32 registers per step in flight). The 64-wide form would run out of
+// registers: it requests the current step's operands at the top of the step, before the next
+// step's x. (Loads return in issue order, so the wait for an operand also waits for every
+// load issued before it: operands requested after the next step's x would make every step
+// wait for that x, a full HBM round trip.)
+constexpr bool l1_ahead(int RC) { return RC <= 32; }
 
 // Inputs of a full bf16 step that the caller loads one step ahead: the lane's 32 x values
 // (16 words of bf16 pairs), two reciprocals and two scales, and (l1_ahead) the step's L1^T
@@ -297,7 +317,7 @@ struct FullIn {
   v4i bw[l1_ahead(RC) ? RC / 16 : 1][4];
 };
 
-template <int RC, class T>
+template <int RC, bool LR, class T>
 __device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xrow, const ActLane& L, int k0,
                                           FullIn<RC>& in) {
   const uint4* src = reinterpret_cast<const uint4*>(xrow + k0 + 32 * L.g);
@@ -308,8 +328,7 @@ __device__ __forceinline__ void load_full(const ActParams& p, const T* __restric
   }
   in.y2 = *reinterpret_cast<const float2*>(p.recip + k0 + 2 * L.lane);
   in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * L.lane);
-  if constexpr (l1_ahead(RC))
-    if (L.nbl > 0) load_l1<RC, T>(p, L, k0, in.bw);
+  if constexpr (l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, in.bw);
 }
 
 // Full bf16 steps, exact path: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein,
@@ -377,7 +396,8 @@ struct StepState {
 // First half of a step: loads, X^ = D(x / scale) and its block maximum.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                           int k0, const FullIn<RC>& in, StepState<DT, RC>& st) {
+                                           int k0, const FullIn<RC>& in, const v4i (&bwc)[RC / 16][4],
+                                           StepState<DT, RC>& st) {
   typedef typename DT::T T;
   constexpr int RW = DT::is_bf16 ? 16 : 32;
   constexpr bool FAST = DT::is_bf16 && FULL;
@@ -403,14 +423,19 @@ __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT
     load_chan<FULL>(p.recip, k, p.M, 1.f, y32);
   }
   // B operands of the down-projection for this step (bf16: with l1_ahead full steps got them
-  // one step ahead with x, other steps load them with their other loads; f32 loads them at the
-  // MFMAs to save registers)
+  // one step ahead with x, other full steps at the top of the step (bwc), the remaining steps
+  // load them with their other loads; f32 loads them at the MFMAs to save registers)
   constexpr int NB = RC / 16;
   if constexpr (FAST && l1_ahead(RC)) {
 #pragma unroll
     for (int n = 0; n < NB; n++)
 #pragma unroll
       for (int c = 0; c < 4; c++) bw[n][c] = in.bw[n][c];
+  } else if constexpr (FAST) {
+#pragma unroll
+    for (int n = 0; n < NB; n++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) bw[n][c] = bwc[n][c];
   } else if (DT::is_bf16 && L.nbl > 0) {
     load_l1<RC, T>(p, L, k0, bw);
   }
@@ -623,13 +648,14 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
 // reciprocals from `in` (loaded by the caller one step ahead); other steps load their own.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                         int k0, v4f* acc, const FullIn<RC>& in) {
+                                         int k0, v4f* acc, const FullIn<RC>& in, const v4i (&bwc)[RC / 16][4]) {
   StepState<DT, RC> st;
-  act_smooth<DT, FMT, NIB, FULL, RC>(p, xrow, L, k0, in, st);
+  act_smooth<DT, FMT, NIB, FULL, RC>(p, xrow, L, k0, in, bwc, st);
   act_finish<DT, FMT, NIB, RC>(p, L, k0, acc, st);
 }
 
-template <class DT, int FMT, bool NIB, int RC>
+// LR: the block has low-rank columns (rank > 0; then every block has at least one 16-wide tile)
+template <class DT, int FMT, bool NIB, int RC, bool LR>
 __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   typedef typename DT::T T;
   constexpr int NW = ACT_WAVES;
@@ -660,7 +686,7 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   FullIn<RC> cur;
   const bool full0 = DT::is_bf16 && k0 < kend && k0 + 128 <= kfull;
   if constexpr (DT::is_bf16)
-    if (full0) load_full<RC>(p, xrow, L, k0, cur);
+    if (full0) load_full<RC, LR>(p, xrow, L, k0, cur);
 
   L.sx = 0.f;
   L.ysx = 0.f;
@@ -682,24 +708,29 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   for (int n = 0; n < RC / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // full steps first (k0 ascending), then the tail and padding; bf16 full steps load the next
-  // step's x and reciprocals before computing the current one
+  // step's x and reciprocals before computing the current one. Those loads are issued whether
+  // or not a next step exists (the last step reloads its own columns, unused), so that the
+  // compiler's wait for the current step's operands leaves them in flight.
+  v4i bwc[RC / 16][4];  // the current full step's L1^T operands when they do not travel ahead
   if constexpr (DT::is_bf16) {
     if (full0) {
       for (;;) {
         const int kn = k0 + 128 * NW;
         const bool more = kn < kend && kn + 128 <= kfull;
+        if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
         FullIn<RC> nxt;
-        if (more) load_full<RC>(p, xrow, L, kn, nxt);
-        act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur);
+        load_full<RC, LR>(p, xrow, L, more ? kn : k0, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
+        act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
         k0 = kn;
         if (!more) break;
         cur = nxt;
       }
     }
   } else {
-    for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur);
+    for (; k0 < kend && k0 + 128 <= kfull; k0 += 128 * NW) act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
   }
-  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false, RC>(p, xrow, L, k0, acc, cur);
+  for (; k0 < kend; k0 += 128 * NW) act_step<DT, FMT, NIB, false, RC>(p, xrow, L, k0, acc, cur, bwc);
 
   if (L.nbl > 0) {
     // fixed-order sum of the waves' partial down-projections
@@ -817,14 +848,18 @@ hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_bloc
   const dim3 grid(row_blocks, p.k_chunks, r_chunks);
   const int threads = 64 * ACT_WAVES;
   const bool nib = fmt == SVDQ_FMT_MX || p.bits <= 4;
-#define SVDQ_ACT(DT, FMT, NIB)                                       \
-  do {                                                                \
-    if (rchunk == 16)                                                 \
-      k_act_quant<DT, FMT, NIB, 16><<<grid, threads, 0, stream>>>(p); \
-    else                                                              \
-      k_act_quant<DT, FMT, NIB, 64><<<grid, threads, 0, stream>>>(p); \
+#define SVDQ_ACT(DT, FMT, NIB)                                             \
+  do {                                                                      \
+    if (p.rp == 0)                                                          \
+      k_act_quant<DT, FMT, NIB, 16, false><<<grid, threads, 0, stream>>>(p); \
+    else if (rchunk == 16)                                                  \
+      k_act_quant<DT, FMT, NIB, 16, true><<<grid, threads, 0, stream>>>(p);  \
+    else if (rchunk == 32)                                                  \
+      k_act_quant<DT, FMT, NIB, 32, true><<<grid, threads, 0, stream>>>(p);  \
+    else                                                                    \
+      k_act_quant<DT, FMT, NIB, 64, true><<<grid, threads, 0, stream>>>(p);  \
   } while (0)
-  if (!p.recip || (rchunk != 16 && rchunk != 64)) return hipErrorInvalidValue;
+  if (!p.recip || (rchunk != 16 && rchunk != 32 && rchunk != 64)) return hipErrorInvalidValue;
   if (dtype == SVDQ_BF16) {
     if (fmt == SVDQ_FMT_MX)
       SVDQ_ACT(BF16, SVDQ_FMT_MX, true);

@@ -161,17 +161,28 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
       }
     }
   };
+  // The first batch is peeled: its loads go out before the up-projection's operands are summed
+  // and multiplied (inside a loop the compiler would hoist that sum, and its wait, above them).
   int s = s0;
+  if (s + DEC_BATCH <= s1) {
+    Batch bt;
+    batch_load(bt, s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (up0) up_mma(u0, kk0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < DEC_BATCH; u++) step(bt.wv[u], bt.wsc[u], bt.av[u], bt.asc[u]);
+    s += DEC_BATCH;
+  } else if (up0) {
+    up_mma(u0, kk0);  // no full batch
+  }
   for (; s + DEC_BATCH <= s1; s += DEC_BATCH) {
     Batch bt;
     batch_load(bt, s);
     __builtin_amdgcn_sched_barrier(0);
-    if (s == s0 && up0) up_mma(u0, kk0);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < DEC_BATCH; u++) step(bt.wv[u], bt.wsc[u], bt.av[u], bt.asc[u]);
   }
-  if (s == s0 && up0) up_mma(u0, kk0);  // no full batch
   for (; s < s1; s++) {
     v4i wv[2], av[MT];
     u32 wsc[2], asc[MT];

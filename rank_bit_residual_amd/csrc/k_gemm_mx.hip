@@ -230,12 +230,28 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
         for (int j = 0; j < C::NT; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u.a[h][i], u.b[h][j], acc[i][j], 0, 0, 0);
   };
+  // A finished down (no split-K partials) is requested with plain loads before the first stages
+  // go out, so their wait before the MFMAs leaves the stages in flight; partials are summed as
+  // they arrive, so they are requested after the stages. Every launch has at least two stages.
   UpOps u0;
-  if (p.rp > 0) up_load(u0, 0);
+  const bool up_direct = p.down_chunks <= 1;
+  if (p.rp > 0 && up_direct) {
 #pragma unroll
-  for (int s = 0; s < C::DIST; s++)
-    if (s < nst) issue(s);
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+        u0.a[h][i] = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const T*>(p.down) + (int64_t)drow[i] * p.rp + 16 * h + 8 * g));
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+        u0.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + 16 * h + 8 * g));
+    }
+  }
+  static_assert(C::DIST == 2, "two stages issued here");
+  issue(0);
+  issue(1);
   if (p.rp > 0) {
+    if (!up_direct) up_load(u0, 0);
     up_mma(u0);
     for (int kk = 32; kk < p.rp; kk += 32) {
       UpOps u;

@@ -55,7 +55,7 @@ enum { WS_CODES = 0, WS_SCALES, WS_DOWN, WS_PARTIAL, WS_AMAX, WS_SX, WS_RECIP, W
 struct LaunchPlan {
   int64_t B;
   int row_blocks;   // activation row blocks of kernel (a) (16 rows each)
-  int rchunk;       // low-rank columns per block of kernel (a): 64, or 16 for small batches
+  int rchunk;       // low-rank columns per block of kernel (a): 32 (rank <= 32) or 64, 16 for small batches
   int r_chunks;     // rchunk-wide low-rank column chunks of kernel (a)
   int k_chunks;     // split of K in kernel (a) (down-projection partials when > 1)
   int k_chunk_len;  // K columns per chunk (multiple of 128)

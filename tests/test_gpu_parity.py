@@ -473,6 +473,28 @@ def test_mx_large_batch_shapes(B, M, N, rank):
     assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,M,N,rank", [
+    (4096, 1024, 4352, 32),   # 272 tiles of 256 x 256 over 256 blocks: some blocks take two
+    (4100, 768, 4032, 64),    # 357 ragged 256 x 192 tiles (17 x 21): partial tiles inside a block's list
+    (2048, 512, 12288, 96),   # 384 tiles, three up-projection stages per tile
+])
+def test_mx_large_batch_several_tiles_per_block(B, M, N, rank):
+    """More output tiles than compute units: each block of the large-batch kernel walks several
+    tiles, storing all but its last straight from the registers."""
+    assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]
+
+
+def test_mx_exact_special_case_ragged_tiles_per_block():
+    """Rank 0, E2M1-grid operands (exact product) over 357 ragged tiles, several per block."""
+    B, M, N = 4100, 256, 4032
+    assert _gemm_route(B, M, N, "mx", 4, "bf16") == "mx256x192"
+    x, w = _e2m1_exact_operands(np.random.default_rng(77), B, M, N)
+    p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx")
+    y = R.linear(_g(x, "bf16"), p)
+    bad = np.argwhere(_bits(_np(y)) != _bits(O.to_dtype(x @ w, "bf16")))
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
 def test_mx_exact_special_case_large_batch():
     rng = np.random.default_rng(14)
     B, M, N = 520, 320, 392
