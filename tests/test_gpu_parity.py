@@ -474,18 +474,18 @@ def test_mx_large_batch_shapes(B, M, N, rank):
 
 
 @pytest.mark.parametrize("B,M,N,rank", [
-    (4096, 1024, 4352, 32),   # 272 tiles of 256 x 256 over 256 blocks: some blocks take two
-    (4100, 768, 4032, 64),    # 357 ragged 256 x 192 tiles (17 x 21): partial tiles inside a block's list
-    (2048, 512, 12288, 96),   # 384 tiles, three up-projection stages per tile
+    (4096, 1024, 4352, 32),   # 272 tiles of 256 x 256: more tiles than compute units
+    (4100, 768, 4032, 64),    # 357 ragged 256 x 192 tiles (17 x 21), two 32-wide up-projection rounds
+    (2048, 512, 12288, 96),   # 512 tiles of 256 x 192, three up-projection rounds
 ])
 def test_mx_large_batch_several_tiles_per_block(B, M, N, rank):
-    """More output tiles than compute units: each block of the large-batch kernel walks several
-    tiles, storing all but its last straight from the registers."""
+    """More output tiles than compute units (a compute unit runs several tiles in turn), with
+    ragged tiles and ranks above 32, against the oracle."""
     assert _mx_case(B, M, N, rank, B + N) <= TOL["bf16"]
 
 
 def test_mx_exact_special_case_ragged_tiles_per_block():
-    """Rank 0, E2M1-grid operands (exact product) over 357 ragged tiles, several per block."""
+    """Rank 0, E2M1-grid operands (exact product) over 357 ragged tiles, more than compute units."""
     B, M, N = 4100, 256, 4032
     assert _gemm_route(B, M, N, "mx", 4, "bf16") == "mx256x192"
     x, w = _e2m1_exact_operands(np.random.default_rng(77), B, M, N)
