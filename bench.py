@@ -394,8 +394,8 @@ def run_calibrate(args):
 
 def run_prepare(args):
     """One-time preparation of the workload's weight (fold, truncated SVD, residual
-    quantisation and packing): the host route and the route with the SVD's large products on
-    the GPU, timed once each (wall clock, including the blob copy to the device)."""
+    quantisation and packing): the host route and the route with the truncated SVD on the GPU,
+    timed once each (wall clock, including the blob copy to the device)."""
     import numpy as np
     import torch
 

@@ -185,14 +185,18 @@ int svdq_prepared_layout(int64_t M, int64_t N, int64_t rank, int fmt, int bits, 
 int svdq_prepare(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
                  int64_t rank, int fmt, int bits, int dtype, void* blob_host,
                  void* left_out, void* right_out, void* residual_out);
-/* The same preparation with the truncated SVD's large products (the randomized subspace
- * iteration's panel products with the smoothed weight, in float64) on the GPU; the small
- * dense steps, the fold, the residual and the quantisation stay on the host, so the result
- * satisfies the same contract (a best rank-r approximation up to the randomized route's
- * accuracy). Matrices with min(M, N) <= 512 take the host's full Jacobi route and need no
- * workspace. workspace: device, 256-byte aligned, >= svdq_prepare_gpu_workspace_bytes
- * bytes; the call enqueues copies and kernels on `stream` and waits for them (host call).
- * Errors as svdq_prepare, plus EINVAL for a small workspace and EHIP. */
+/* The same preparation with the truncated SVD on the GPU: the randomized subspace iteration
+ * (k = rank + 32 panel columns, 16 power iterations) and its Rayleigh-Ritz step run in float64 on
+ * the device — panel products with the smoothed weight on float64 matrix cores, the panels
+ * orthonormalised by Cholesky-QR twice (the k x k Cholesky factorisations on the host), the
+ * Rayleigh-Ritz one-sided Jacobi on the device; the fold, the residual and the quantisation stay
+ * on the host. The result satisfies the same contract (a best rank-r approximation up to the
+ * randomized route's accuracy) but is not bit-identical to svdq_prepare's. Matrices with
+ * min(M, N) <= 512, or with rank + 32 above 256 panel columns, take the host's split and need no
+ * workspace. workspace: device, 256-byte aligned, >= svdq_prepare_gpu_workspace_bytes bytes
+ * (the float32 weight, three float64 panels of max(M, N) x k, a k x N float64 projection and
+ * k x k matrices); the call enqueues copies and kernels on `stream` and waits for them (host
+ * call). Errors as svdq_prepare, plus EINVAL for a small workspace and EHIP. */
 int svdq_prepare_gpu_workspace_bytes(int64_t M, int64_t N, int64_t rank, size_t* bytes_out);
 int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, const float* scale,
                      int64_t rank, int fmt, int bits, int dtype, void* blob_host,

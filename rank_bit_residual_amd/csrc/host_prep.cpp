@@ -279,8 +279,8 @@ int svdq_prepare_gpu_workspace_bytes(int64_t M, int64_t N, int64_t rank, size_t*
   clear_error();
   if (!bytes_out) return set_error(SVDQ_EINVAL, "bytes_out is NULL");
   if (M < 1 || N < 1 || rank < 0 || rank > std::min(M, N)) return set_error(SVDQ_EINVAL, "bad shape or rank");
-  const int64_t k = host::randomized_panel_columns(M, N, rank);
-  *bytes_out = k ? device_panels_bytes(M, N, k) : 0;
+  const int64_t k = device_svd_columns(M, N, rank);
+  *bytes_out = k ? device_svd_bytes(M, N, k, rank) : 0;
   return SVDQ_OK;
 }
 
@@ -299,7 +299,7 @@ int svdq_prepare_gpu(const void* weight, int64_t M, int64_t N, int64_t ldw, cons
   st = prepare_impl(HostMat{weight, ldw, dtype, false}, M, N, scale, rank, fmt, bits, dtype, blob_host, left_out,
                     right_out, residual_out, &dev);
   if (st) return st;
-  if (dev.hip_error) return set_error(SVDQ_EHIP, "device products of the truncated SVD failed");
+  if (dev.hip_error) return set_error(SVDQ_EHIP, "truncated SVD on the device failed");
   return SVDQ_OK;
 }
 

@@ -310,12 +310,10 @@ void full_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, doub
 }
 
 void randomized_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, int64_t k, int power_iters,
-                    double* L1, double* L2, PanelProducts* dev) {
-  // the large products with A: on the host, or through the backend
+                    double* L1, double* L2) {
+  // the large products with A
   auto prod = [&](int kind, const double* P, double* C) {
-    if (dev)
-      dev->product(kind, k, P, C);
-    else if (kind == 0)
+    if (kind == 0)
       gemm<double, float>(k, N, M, P, M, 1, A, lda, 1, C, N);  // C^T [k x N] = P^T [k x M] * A [M x N]
     else
       gemm<double, float>(k, M, N, P, N, 1, A, 1, lda, C, M);  // C^T [k x M] = P^T [k x N] * A^T [N x M]
@@ -359,14 +357,13 @@ int64_t randomized_panel_columns(int64_t M, int64_t N, int64_t r) {
   return (r <= 0 || n <= 512 || k >= n) ? 0 : k;
 }
 
-void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2,
-                   PanelProducts* dev) {
+void truncated_svd(const float* A, int64_t M, int64_t N, int64_t lda, int64_t r, double* L1, double* L2) {
   if (r <= 0) return;
   const int64_t k = randomized_panel_columns(M, N, r);
   if (k == 0)
     full_svd(A, M, N, lda, r, L1, L2);
   else
-    randomized_svd(A, M, N, lda, r, k, 16, L1, L2, dev);
+    randomized_svd(A, M, N, lda, r, k, 16, L1, L2);
 }
 
 }  // namespace host

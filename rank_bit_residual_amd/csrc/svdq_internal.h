@@ -64,11 +64,15 @@ struct LaunchPlan {
 };
 LaunchPlan make_plan(const Dims& d, int64_t B);
 
-// Truncated SVD with the randomized route's large products on the GPU (k_svd.hip): A [M x N]
-// float32 row-major on the host; workspace: device, >= device_panels_bytes(M, N, k) for
-// k = host::randomized_panel_columns(M, N, r); stream: a hipStream_t. Returns the first HIP
-// error (0 = none); small matrices take the host's full Jacobi route unchanged.
-size_t device_panels_bytes(int64_t M, int64_t N, int64_t k);
+// Truncated SVD on the GPU (k_svd.hip): the randomized route's subspace iteration and
+// Rayleigh-Ritz step in float64 on the device, for A [M x N] float32 row-major on the host.
+// device_svd_columns: the panel width k of that route (0: the host takes the whole split —
+// the full Jacobi route of small matrices, or panels wider than the device route's kMaxDeviceK);
+// workspace: device, >= device_svd_bytes(M, N, k, r); stream: a hipStream_t. Returns the first
+// HIP error (0 = none).
+constexpr int64_t kMaxDeviceK = 256;
+int64_t device_svd_columns(int64_t M, int64_t N, int64_t r);
+size_t device_svd_bytes(int64_t M, int64_t N, int64_t k, int64_t r);
 int run_split_on_device(const float* A, int64_t M, int64_t N, int64_t r, void* workspace, void* stream, double* L1,
                         double* L2);
 void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]);
