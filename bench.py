@@ -99,6 +99,85 @@ def roofline(wl, B, work, gemm_ms, call_ms):
     return roof
 
 
+CEILINGS = os.path.join(ROOT, "profiles", "ceilings.json")
+
+
+def measured_ceiling(wl, roof, path=CEILINGS):
+    """The GEMM's achieved rate against the committed measured ceiling of the same kind (the
+    FP4 or INT8 MFMA loop for MFMA-bound shapes, the HBM read stream for HBM-bound ones), or
+    None when no ceilings were measured."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if roof["bound"] == "mfma":
+        key = "fp4_mfma" if wl.fmt == "mx" else "int8_mfma"
+        peak, unit = c[key]["tflops"], "TFLOP/s"
+    else:
+        key = "hbm_read"
+        peak, unit = c[key]["gbs"], "GB/s"
+    return {"probe": key, "peak": peak, "unit": unit, "frac": roof["achieved"] / peak,
+            "source": os.path.relpath(path, ROOT)}
+
+
+def run_ceilings(args):
+    """Measured ceilings of this GPU (svdq_ceiling): the FP4 and INT8 MFMA loops, a read stream
+    and a device copy over buffers rotated past the 256 MB MALL. One JSON object on stdout."""
+    import torch
+
+    from rank_bit_residual_amd import _lib as L
+
+    lib = L.load()
+    dev = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    scratch = torch.empty(32 << 20, dtype=torch.uint8, device=dev)  # 1 KB per block of the widest read stream
+
+    def per_launch(fn, n):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    out = {"device": torch.cuda.get_device_name(dev)}
+    work = ctypes.c_double()
+    for kind, name in ((0, "fp4_mfma"), (1, "int8_mfma")):
+        iters = 20000
+
+        def launch(_, kind=kind, iters=iters):
+            L.check(lib.svdq_ceiling(kind, iters, None, 0, ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), stream,
+                                     ctypes.byref(work)))
+
+        t = per_launch(launch, 10)
+        out[name] = {"tflops": work.value / t / 1e12, "launch_us": t * 1e6, "iterations": iters}
+        print(f"{name}: {out[name]['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    nbuf, size = 4, 256 << 20
+    bufs = [torch.full((size,), i + 1, dtype=torch.uint8, device=dev) for i in range(nbuf)]
+    best = None
+    for blocks in (2048, 8192, 32768):
+        def launch(i, blocks=blocks):
+            b = bufs[i % nbuf]
+            L.check(lib.svdq_ceiling(2, blocks, ctypes.c_void_p(b.data_ptr()), size,
+                                     ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), stream, ctypes.byref(work)))
+
+        t = per_launch(launch, 20)
+        gbs = work.value / t / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": gbs, "blocks": blocks, "bytes_per_launch": work.value, "launch_us": t * 1e6}
+    out["hbm_read"] = best
+    print(f"hbm_read: {best['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    dst = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    t = per_launch(lambda i: dst[i % nbuf].copy_(bufs[(i + 1) % nbuf]), 20)
+    out["copy"] = {"gbs": 2 * size / t / 1e9, "bytes_per_launch": 2 * size, "launch_us": t * 1e6}
+    out["command"] = "python bench.py --ceilings"
+    print(json.dumps(out), flush=True)
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -295,6 +374,7 @@ def run(args):
     roof["traffic"] = pmc_traffic(wl, B)
     if roof["bound"] == "mfma":
         roof["mfma_util"] = pmc_mfma_util(wl, B)  # counter evidence: MFMA busy / active cycles
+    roof["measured_ceiling"] = measured_ceiling(wl, roof)
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -540,6 +620,8 @@ def main():
                     help="time the one-time weight preparation on the host and with the GPU SVD products")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the smoothing-scale calibration on the workload's x and W instead of the operator")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the chip's FP4/INT8 MFMA, HBM read and copy ceilings (one JSON line)")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -570,7 +652,9 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    if args.prepare:
+    if args.ceilings:
+        run_ceilings(args)
+    elif args.prepare:
         run_prepare(args)
     elif args.toy_experiment:
         print(json.dumps(toy_experiment()), flush=True)

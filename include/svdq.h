@@ -353,6 +353,24 @@ int svdq_profile_begin(int max_calls, unsigned stage_mask);
 int svdq_profile_begin_sampled(int max_calls, unsigned stage_mask, int every); /* EINVAL if every < 1 */
 int svdq_profile_end(float* ms, int cap, int* n_calls);
 
+/* --------------------------------------------------------------------------------------
+ * Measured ceilings (measurement aid; not on any page): kernels that run what the operator's
+ * kernels are bound by, with nothing else, so that their times can be reported against what
+ * the chip sustains as well as against its datasheet peaks.
+ *   kind 0: a loop of v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands (unit scales) on
+ *     register operands, two waves per SIMD, eight independent accumulators per wave;
+ *     arg = loop iterations (>= 1).
+ *   kind 1: the same with v_mfma_i32_32x32x32_i8; arg = loop iterations.
+ *   kind 2: a grid-stride read of buf[0, buf_bytes) (device, 16-byte aligned, >= 16 bytes) in
+ *     16-byte loads by arg 256-thread blocks (1 .. 2^20); buf_bytes rounded down to 16.
+ * out: device float32 scratch of out_bytes bytes (kinds 0-1: 8 floats per compute unit;
+ * kind 2: 1 KB per block); its contents are unspecified afterwards. work_out (host): flops
+ * (kinds 0-1) or bytes (kind 2) of the launch. One kernel on `stream`; asynchronous.
+ * Errors: EINVAL for an unknown kind, an argument out of range, NULL or short buffers; EHIP.
+ * ------------------------------------------------------------------------------------ */
+int svdq_ceiling(int kind, int64_t arg, const void* buf, size_t buf_bytes, float* out, size_t out_bytes,
+                 svdq_stream_t stream, double* work_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ SIGNATURES = {
     "svdq_profile_begin": (c_int, [c_int, ctypes.c_uint]),
     "svdq_profile_begin_sampled": (c_int, [c_int, ctypes.c_uint, c_int]),
     "svdq_profile_end": (c_int, [ctypes.POINTER(ctypes.c_float), c_int, ctypes.POINTER(c_int)]),
+    "svdq_ceiling": (c_int, [c_int, ctypes.c_int64, c_vp, ctypes.c_size_t, c_vp, ctypes.c_size_t, c_vp,
+                             ctypes.POINTER(ctypes.c_double)]),
 }
 NSTAGES = 4
 STAGE_NAMES = ("amax", "act_quant_down", "down_reduce", "gemm")

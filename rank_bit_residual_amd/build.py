@@ -30,6 +30,7 @@ HIP_SOURCES = {
     "k_gemm_int.hip": [],
     "k_calib.hip": [],
     "k_svd.hip": [],
+    "k_ceiling.hip": [],
     "capi.hip": [],
 }
 CXX = os.environ.get("CXX", "g++")

@@ -480,6 +480,21 @@ int svdq_profile_begin_sampled(int max_calls, unsigned stage_mask, int every) {
   return SVDQ_OK;
 }
 
+int svdq_ceiling(int kind, int64_t arg, const void* buf, size_t buf_bytes, float* out, size_t out_bytes,
+                 svdq_stream_t stream, double* work_out) {
+  clear_error();
+  clear_stale_hip_error();
+  if (kind < 0 || kind > 2) return set_error(SVDQ_EINVAL, "kind must be 0 (FP4 MFMA), 1 (INT8 MFMA) or 2 (read stream)");
+  if (!out || !work_out) return set_error(SVDQ_EINVAL, "NULL buffer");
+  if (!aligned(out, 4)) return set_error(SVDQ_EINVAL, "misaligned buffer");
+  double work = 0.0;
+  const hipError_t e = launch_ceiling(kind, arg, buf, buf_bytes, out, out_bytes, (hipStream_t)stream, &work);
+  if (e == hipErrorInvalidValue)
+    return set_error(SVDQ_EINVAL, "iterations or blocks out of range, or a buffer too small or misaligned");
+  if (e == hipSuccess) *work_out = work;
+  return hip_status(e, "ceiling launch");
+}
+
 int svdq_profile_end(float* ms, int cap, int* n_calls) {
   clear_error();
   if (!g_prof.open) return set_error(SVDQ_EINVAL, "no profiling session is open");

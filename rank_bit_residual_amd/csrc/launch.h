@@ -104,4 +104,9 @@ hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_
 // MXFP4, bf16, B <= 64: K split over waves, weights streamed straight into registers.
 hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream);
 
+// Ceiling probes (k_ceiling.hip): kind 0 FP4 MFMA loop, 1 INT8 MFMA loop (arg = iterations),
+// 2 read stream over buf[0, bytes) (arg = 256-thread blocks); *work = flops or bytes of one launch.
+hipError_t launch_ceiling(int kind, int64_t arg, const void* buf, size_t bytes, float* out, size_t out_bytes,
+                          hipStream_t stream, double* work);
+
 }  // namespace svdq

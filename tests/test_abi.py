@@ -60,6 +60,11 @@ def test_host_calls_report_errors_without_a_gpu():
     assert b"every" in lib.svdq_last_error()
     n = ctypes.c_int()
     assert lib.svdq_profile_end(None, 0, ctypes.byref(n)) == _lib.SVDQ_EINVAL  # no open session
+    # ceiling probes: an unknown kind or a NULL buffer is refused before any HIP call
+    work = ctypes.c_double()
+    assert lib.svdq_ceiling(3, 1, None, 0, None, 0, None, ctypes.byref(work)) == _lib.SVDQ_EINVAL
+    assert b"kind" in lib.svdq_last_error()
+    assert lib.svdq_ceiling(0, 1, None, 0, None, 0, None, ctypes.byref(work)) == _lib.SVDQ_EINVAL
 
 
 def test_int_shapes_beyond_exact_int32_accumulation_are_refused():

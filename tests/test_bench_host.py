@@ -101,3 +101,21 @@ def test_default_workload_is_the_largest(monkeypatch):
     assert bench.main() == 0 and seen["w"] == 4
     flops = {c: WORKLOADS[c].B * WORKLOADS[c].M * WORKLOADS[c].N for c in WORKLOADS}
     assert max(flops, key=flops.get) == 4
+
+
+def test_measured_ceiling(tmp_path):
+    """The GEMM's rate against the committed measured ceiling of its own kind: the FP4 loop for
+    MXFP4 shapes, the INT8 loop for INT ones, the read stream for HBM-bound shapes; none
+    without a ceilings file."""
+    import json
+
+    c = {"fp4_mfma": {"tflops": 8000.0}, "int8_mfma": {"tflops": 4000.0}, "hbm_read": {"gbs": 5000.0}}
+    path = tmp_path / "ceilings.json"
+    path.write_text(json.dumps(c))
+    for cid, probe, peak in ((4, "fp4_mfma", 8000.0), (2, "int8_mfma", 4000.0), (5, "hbm_read", 5000.0)):
+        wl = WORKLOADS[cid]
+        r = bench.roofline(wl, wl.B, bench.algorithmic(wl, wl.B), 0.05, 0.06)
+        m = bench.measured_ceiling(wl, r, str(path))
+        assert m["probe"] == probe and m["peak"] == peak
+        assert m["frac"] == pytest.approx(r["achieved"] / peak)
+    assert bench.measured_ceiling(WORKLOADS[4], r, str(tmp_path / "absent.json")) is None

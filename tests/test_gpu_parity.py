@@ -7,6 +7,8 @@ the oracle's float64 forward on the library's own exported factors and residual;
 special cases (rank 0, unit scale, values the quantiser reproduces exactly) must match
 x @ W bit for bit.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -822,3 +824,28 @@ def test_parity_shape_sweep(c, B, M, N, rank, fmt, bits, dtype, bias):
     err = O.rel_fro(_np(y), ref)
     print(f"case {c}: rel Frobenius error {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+# ----------------------------------------------------------------------------- measured ceilings
+def test_ceiling_probes_run_and_count_their_work():
+    """svdq_ceiling: the FP4 and INT8 MFMA loops and the read stream run through the C ABI and
+    report the work of one launch (flops: CUs x 2 blocks x 4 waves x iterations x 8 MFMAs x
+    the instruction's flops; bytes: the buffer rounded down to 16)."""
+    lib = _lib.load()
+    d = dev()
+    cus = torch.cuda.get_device_properties(d).multi_processor_count
+    scratch = torch.empty(1 << 22, dtype=torch.uint8, device=d)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(d).cuda_stream)
+    work = ctypes.c_double()
+    for kind, per in ((0, 2 * 32 * 32 * 64), (1, 2 * 32 * 32 * 32)):
+        assert lib.svdq_ceiling(kind, 3, None, 0, ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), stream,
+                                ctypes.byref(work)) == 0, lib.svdq_last_error()
+        assert work.value == cus * 2 * 4 * 3 * 8 * per
+    buf = torch.arange(1 << 20, dtype=torch.int32, device=d)
+    assert lib.svdq_ceiling(2, 64, ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4 + 7,
+                            ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), stream, ctypes.byref(work)) == 0
+    assert work.value == buf.numel() * 4
+    # a scratch buffer too small for the launch is refused
+    assert lib.svdq_ceiling(2, 1 << 14, ctypes.c_void_p(buf.data_ptr()), 1024, ctypes.c_void_p(scratch.data_ptr()),
+                            1024, stream, ctypes.byref(work)) == _lib.SVDQ_EINVAL
+    torch.cuda.synchronize()
