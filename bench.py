@@ -39,7 +39,7 @@ def gemm_kernel(wl, B):
     """(kernel name, source file) of the residual GEMM that svdq_linear launches for this shape."""
     if wl.fmt == "mx" and wl.dtype == "bf16" and B <= 64:
         return "k_gemm_decode_mx", os.path.join(CSRC, "k_gemm_decode.hip")
-    if wl.fmt == "mx" and wl.dtype == "bf16" and B >= 256:
+    if wl.fmt == "mx" and wl.dtype == "bf16" and B > 64:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
     kp = -(-wl.M // 256) * 256
     if wl.fmt == "int" and wl.bits <= 4 and kp // 256 >= 6:  # the INT4 kernel keeps 6 stages of 256 codes in flight

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   static_assert(C::NS >= C::DIST + 2, "ring too shallow for the prefetch distance");
   constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
   constexpr int NM = C::MT * C::NT;  // MFMAs per slice
-  static_assert(NM > NR, "the interleave schedule assumes more MFMAs than operand reads per slice");
+  constexpr int P1 = NM - 1 < NR ? NM - 1 : NR;  // slice-1 reads paired with slice-0 MFMAs
   const int nst = p.kstages;
 
   // ---- up-projection first: acc = down L2 on bf16 32x32x16 MFMAs. Its first 32 rank columns
@@ -275,14 +275,15 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const uint8_t* base = smem + (s % C::NS) * C::STAGE;
     read_frag(base, 1, f1);
     mma(cur0, scur, 0);
-    // slice 1's reads one per slice-0 MFMA
+    // slice 1's reads one per slice-0 MFMA (after the first); reads beyond the MFMAs go last
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-    for (int q = 0; q < NR; q++) {
+    for (int q = 0; q < P1; q++) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR - 1, 0);
+    if constexpr (NR > P1) __builtin_amdgcn_sched_group_barrier(0x100, NR - P1, 0);
+    if constexpr (NM - 1 > P1) __builtin_amdgcn_sched_group_barrier(0x008, NM - 1 - P1, 0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (AHEAD >= 0) {
       wait_vmcnt<C::LOADS_PER_STAGE * AHEAD>();
@@ -410,12 +411,14 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
   return launch_gemm_kernel(k_gemm_mx<BF16, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
-// Large-batch MXFP4 path for bf16 inputs; returns hipErrorNotSupported when the shape or dtype
-// is not covered, so the caller falls back to the general kernel.
+// MXFP4 path for bf16 inputs above decode batches (B > 64); returns hipErrorNotSupported when
+// the shape or dtype is not covered, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
-  if (dtype != SVDQ_BF16 || p.B < 256 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
+  if (dtype != SVDQ_BF16 || p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
   // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
-  // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192).
+  // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192). Batches of
+  // at most 128 rows take 128-row tiles: half the padded rows' MFMAs and operand bytes.
+  if (p.B <= 128) return p.N % 256 != 0 && p.N % 192 == 0 ? launch_mx_t<128, 192>(p, stream) : launch_mx_t<128, 256>(p, stream);
   const int tiles_m = (p.B + 255) / 256;
   if (p.N % 256 == 0 && tiles_m * (p.N / 256) >= 512) return launch_mx_t<256, 256>(p, stream);
   if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, stream);

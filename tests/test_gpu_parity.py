@@ -250,7 +250,9 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
     kp = -(-M // 256) * 256
     if fmt == "mx" and dtype == "bf16" and B <= 64:
         return "decode"
-    if fmt == "mx" and dtype == "bf16" and B >= 256:
+    if fmt == "mx" and dtype == "bf16" and B <= 128:
+        return "mx128x192" if N % 256 != 0 and N % 192 == 0 else "mx128x256"
+    if fmt == "mx" and dtype == "bf16":
         tiles_m = -(-B // 256)
         if N % 256 == 0 and tiles_m * (N // 256) >= 512:
             return "mx256x256"
@@ -298,6 +300,10 @@ def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
 
 @pytest.mark.parametrize("B,M,N,route", [
     (520, 512, 576, "mx256x192"),    # the attention-projection tile (N a multiple of 192), ragged B
+    (200, 512, 392, "mx256x256"),    # 128 < B < 256: one 256-row tile with 56 padded rows
+    (100, 512, 576, "mx128x192"),    # B <= 128: 128-row tiles, N a multiple of 192
+    (128, 768, 512, "mx128x256"),    # one full 128-row tile
+    (65, 256, 300, "mx128x256"),     # one live row past the decode range, ragged N
     (4096, 256, 8192, "mx256x256"),  # 512 tiles of 256 x 256: the MLP up-projection's tile choice
     (16, 1024, 392, "decode"),       # decode kernel, one 16-row tile, eight waves
     (17, 1280, 200, "decode"),       # decode kernel, two row tiles (the second with one live row)
