@@ -42,7 +42,8 @@ def gemm_kernel(wl, B):
     if wl.fmt == "mx" and wl.dtype == "bf16" and B > 64:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
     kp = -(-wl.M // 256) * 256
-    if wl.fmt == "int" and wl.bits <= 4 and kp // 256 >= 6:  # the INT4 kernel keeps 6 stages of 256 codes in flight
+    # the INT kernel keeps 6 stages in flight: 256 nibble codes (<= 4 bits) or 128 int8 codes each
+    if wl.fmt == "int" and (kp // 256 if wl.bits <= 4 else kp // 128) >= 6:
         return "k_gemm_int4", os.path.join(CSRC, "k_gemm_int.hip")
     return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 

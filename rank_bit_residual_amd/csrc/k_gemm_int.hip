@@ -1,4 +1,4 @@
-// Residual GEMM for per-tensor INT codes of up to 4 bits on gfx950 (step (c) of the operator):
+// Residual GEMM for per-tensor INT codes on gfx950 (step (c) of the operator):
 //   Y = D( s_x s_R (Q(X^) Q(R)) + down L2 )
 // with exact integer products on v_mfma_i32_32x32x32_i8 and the up-projection on bf16 (or
 // fp32) MFMAs into the dequantised fp32 accumulators.
@@ -7,7 +7,8 @@
 // item 3 (per-tensor INT quantisation; Y = (X^ L1) L2 + Q(X^) Q(R)); "flashinfer.gemm.
 // svdquant_linear" (the residual GEMM with the up-projection in its epilogue).
 //
-// Codes arrive as two's-complement nibbles (even k in the low nibble). The matrix cores take
+// Codes of at most 4 bits arrive as two's-complement nibbles (even k in the low nibble; codes of
+// 5-8 bits as int8 bytes, which go to the matrix cores unchanged). The matrix cores take
 // int8, and a nibble c placed in the high half of a byte reads as the int8 16 c: per 32-bit
 // word, w & 0xF0F0F0F0 gives the odd codes and (w << 4) & 0xF0F0F0F0 the even ones, times 16.
 // Products are then 256 times the code products (|sum| <= 256 * 64 * K stays far below
@@ -66,7 +67,9 @@ __device__ inline v4i nib16(u32 w0, u32 w1) {
              (int)(w1 & 0xF0F0F0F0u)};
 }
 
-template <class DT>
+// NIB: codes are nibbles (bits <= 4; 256 codes per 128-byte stage, unpacked to 16 x code);
+// otherwise int8 codes (5-8 bits; 128 codes per stage, fed to the matrix cores as stored).
+template <class DT, bool NIB>
 __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   using namespace gi;
   typedef typename DT::T T;
@@ -159,8 +162,29 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   };
   // one stage; AHEAD = stages issued after s + 1, or -1 for the last stage. The second half's
   // unpacking runs under the first half's MFMAs, the next stage's LDS reads under the second's.
+  // int8 codes: one 32-code MFMA step per stage, which runs under the next stage's LDS reads.
   auto stage = [&](int s, const Ops& cur, Ops& nxt, auto ahead_c) {
     constexpr int AHEAD = decltype(ahead_c)::value;
+    if constexpr (!NIB) {
+      if constexpr (AHEAD >= 0) {
+        wait_vmcnt<LOADS_PER_STAGE * AHEAD>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        read_stage(s + 1, nxt);
+      }
+      Unp u;
+#pragma unroll
+      for (int i = 0; i < 2; i++) u.a[i] = cur.a[i];
+#pragma unroll
+      for (int j = 0; j < 2; j++) u.b[j] = cur.b[j];
+      mfma4(u);
+      if constexpr (AHEAD >= 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the four LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     Unp u0, u1;
     unpack(cur, 0, u0);
     mfma4(u0);
@@ -264,7 +288,7 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
 #pragma unroll
     for (int w = 1; w < 4; w++) sum += part[((w * 4 + wave) * 4 + v4) * 64 + lane];
 #pragma unroll
-    for (int e = 0; e < 4; e++) f[4 * v4 + e] = ((float)sum[e] * 0x1p-8f) * scl;
+    for (int e = 0; e < 4; e++) f[4 * v4 + e] = ((float)sum[e] * (NIB ? 0x1p-8f : 1.0f)) * scl;
   }
 
   // ---- up-projection into the fp32 accumulators
@@ -325,24 +349,25 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
 
 using namespace dev;
 
-template <class DT>
+template <class DT, bool NIB>
 static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
   const int tiles = ((p.B + gi::BM - 1) / gi::BM) * ((p.N + gi::BN - 1) / gi::BN);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int4<DT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int4<DT, NIB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, gi::SMEM);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  return launch_gemm_kernel(k_gemm_int4<DT>, dim3(tiles), dim3(256), gi::SMEM, stream, p);
+  return launch_gemm_kernel(k_gemm_int4<DT, NIB>, dim3(tiles), dim3(256), gi::SMEM, stream, p);
 }
 
-// Per-tensor INT with codes of at most 4 bits (nibbles); other formats fall back.
+// Per-tensor INT: nibble codes (at most 4 bits) or int8 codes (5-8 bits), with at least DIST
+// K stages; shorter K falls back to the general kernel.
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
-  if (bits > 4 || p.kstages < gi::DIST) return hipErrorNotSupported;
-  if (dtype == SVDQ_BF16) return launch_int4_t<BF16>(p, stream);
-  return launch_int4_t<F32>(p, stream);
+  if (p.kstages < gi::DIST) return hipErrorNotSupported;
+  if (bits <= 4) return dtype == SVDQ_BF16 ? launch_int4_t<BF16, true>(p, stream) : launch_int4_t<F32, true>(p, stream);
+  return dtype == SVDQ_BF16 ? launch_int4_t<BF16, false>(p, stream) : launch_int4_t<F32, false>(p, stream);
 }
 
 }  // namespace svdq

@@ -257,8 +257,8 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
         if N % 256 == 0 and tiles_m * (N // 256) >= 512:
             return "mx256x256"
         return "mx256x192" if N % 192 == 0 else "mx256x256"
-    if fmt == "int" and bits <= 4 and kp // 256 >= 6:
-        return "int4"
+    if fmt == "int" and (kp // 256 if bits <= 4 else kp // 128) >= 6:
+        return "int4" if bits <= 4 else "int8"
     return "generic"
 
 
@@ -279,14 +279,19 @@ def _e2m1_exact_operands(rng, B, M, N):
     (256, 4096, 4096, 4, "bf16"),   # the INT4 workload's shape: 64 x 64 tiles, 16 K stages
     (130, 1792, 200, 3, "f32"),     # 7 stages (one odd steady iteration), ragged B and N, float32 io
     (70, 1536, 328, 2, "bf16"),     # exactly the 6 stages kept in flight, ragged N tile
+    (130, 768, 200, 8, "bf16"),     # int8 codes: exactly 6 stages of 128 codes, ragged B and N
+    (64, 2048, 328, 6, "f32"),      # int8 codes, 16 stages, float32 io
+    (300, 896, 136, 5, "bf16"),     # int8 codes, 7 stages (one odd steady iteration)
 ])
 def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
-    """Rank 0, unit scale, integer x and W with max |.| = qmax through the INT4 kernel (K of at
-    least six 256-code stages): s_x = s_R = 1 and Y = x @ W bit for bit. |Y| <= qmax^2 K < 2^24,
-    so the float32 result is exact and the bf16 one is its single rounding."""
-    assert _gemm_route(B, M, N, "int", bits, dtype) == "int4"
-    rng = np.random.default_rng(B + M + bits)
+    """Rank 0, unit scale, integer x and W with max |.| = qmax through the INT kernel (K of at
+    least six stages of 256 nibble codes or 128 int8 codes): s_x = s_R = 1 and Y = x @ W bit for
+    bit. |Y| <= qmax^2 K < 2^24, so the float32 result is exact and the bf16 one is its single
+    rounding."""
     q = 2 ** (bits - 1) - 1
+    assert q * q * M < 2 ** 24
+    assert _gemm_route(B, M, N, "int", bits, dtype) == ("int4" if bits <= 4 else "int8")
+    rng = np.random.default_rng(B + M + bits)
     x = rng.integers(-q, q + 1, (B, M)).astype(np.float32)
     w = rng.integers(-q, q + 1, (M, N)).astype(np.float32)
     x[0, 0] = w[0, 0] = q
