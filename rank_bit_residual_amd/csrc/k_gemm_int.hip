@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   typedef typename DT::T T;
   extern __shared__ __align__(1024) uint8_t smem[];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the wave index in a scalar register: the DMA loads' LDS destinations are scalar arithmetic
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- tile order: blocks i, i+8, ... share an XCD; within an XCD the row tiles of one

@@ -58,7 +58,9 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   typedef typename DT::T T;
   extern __shared__ __align__(1024) uint8_t smem[];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the wave index is uniform across the wave: kept in a scalar register, so that the LDS
+  // destinations of the DMA loads are computed on the scalar unit
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int l32 = lane & 31, g = lane >> 5;
 
