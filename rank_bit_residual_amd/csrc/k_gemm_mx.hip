@@ -149,26 +149,33 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   struct Scales {
     u32 a[C::MT], b[C::NT];
   };
+  // Per-lane byte offsets of the operand reads within a stage buffer, for the two 64-code
+  // slices: rows 32 apart share the swizzle (it depends on (row >> 2) & 3), so a wave's MT (NT)
+  // rows are one offset plus multiples of 2 KB, immediate offsets of the LDS reads.
+  int fa_off[2], fb_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++) {
+    fa_off[ks] = lds_swz(wm * C::TM + l32, 2 * ks + g);
+    fb_off[ks] = C::A_BYTES + lds_swz(wn * C::TN + l32, 2 * ks + g);
+  }
+  const int sa_lane = s_off_a + (wm * C::TM + l32) * 4, sb_lane = s_off_b + (wn * C::TN + l32) * 4;
   auto read_frag = [&](const uint8_t* base, int ks, Frag& f) {
-    const int ch = 2 * ks + g;  // this lane's 32-code K block within the stage
 #pragma unroll
     for (int i = 0; i < C::MT; i++) {
-      const v4i a4 = *reinterpret_cast<const v4i*>(base + lds_swz(wm * C::TM + 32 * i + l32, ch));
+      const v4i a4 = *reinterpret_cast<const v4i*>(base + fa_off[ks] + 2048 * i);
       f.a[i] = v8i{a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < C::NT; j++) {
-      const v4i b4 = *reinterpret_cast<const v4i*>(base + C::A_BYTES + lds_swz(wn * C::TN + 32 * j + l32, ch));
+      const v4i b4 = *reinterpret_cast<const v4i*>(base + fb_off[ks] + 2048 * j);
       f.b[j] = v8i{b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
     }
   };
   auto read_scales = [&](const uint8_t* base, Scales& sc) {
 #pragma unroll
-    for (int i = 0; i < C::MT; i++)
-      sc.a[i] = *reinterpret_cast<const u32*>(base + s_off_a + (wm * C::TM + 32 * i + l32) * 4);
+    for (int i = 0; i < C::MT; i++) sc.a[i] = *reinterpret_cast<const u32*>(base + sa_lane + 128 * i);
 #pragma unroll
-    for (int j = 0; j < C::NT; j++)
-      sc.b[j] = *reinterpret_cast<const u32*>(base + s_off_b + (wn * C::TN + 32 * j + l32) * 4);
+    for (int j = 0; j < C::NT; j++) sc.b[j] = *reinterpret_cast<const u32*>(base + sb_lane + 128 * j);
   };
   auto mma = [&](const Frag& f, const Scales& sc, int ks) {
     const int sh = 8 * (2 * ks + g);
