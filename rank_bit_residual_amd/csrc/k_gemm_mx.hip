@@ -171,21 +171,27 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
       f.b[j] = v8i{b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
     }
   };
+  // A scale word holds the E8M0 bytes of the stage's four 32-code blocks; lane (l32, g) uses
+  // block 2 ks + g in slice ks, so its word is shifted right by 8 g once, and the MFMA picks
+  // byte 2 ks of it (the instruction's scale byte select).
+  const int gsh = 8 * g;
   auto read_scales = [&](const uint8_t* base, Scales& sc) {
 #pragma unroll
-    for (int i = 0; i < C::MT; i++) sc.a[i] = *reinterpret_cast<const u32*>(base + sa_lane + 128 * i);
+    for (int i = 0; i < C::MT; i++) sc.a[i] = *reinterpret_cast<const u32*>(base + sa_lane + 128 * i) >> gsh;
 #pragma unroll
-    for (int j = 0; j < C::NT; j++) sc.b[j] = *reinterpret_cast<const u32*>(base + sb_lane + 128 * j);
+    for (int j = 0; j < C::NT; j++) sc.b[j] = *reinterpret_cast<const u32*>(base + sb_lane + 128 * j) >> gsh;
   };
-  auto mma = [&](const Frag& f, const Scales& sc, int ks) {
-    const int sh = 8 * (2 * ks + g);
+  auto mma = [&](const Frag& f, const Scales& sc, auto ks_c) {
+    constexpr int KS = decltype(ks_c)::value;
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
       for (int j = 0; j < C::NT; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 0,
-                                                                    (int)(sc.a[i] >> sh), 0, (int)(sc.b[j] >> sh));
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * KS, (int)sc.a[i],
+                                                                    2 * KS, (int)sc.b[j]);
   };
+  typedef std::integral_constant<int, 0> Slice0;
+  typedef std::integral_constant<int, 1> Slice1;
 
   // Pipeline: stage s+DIST is issued into the ring at the top of iteration s; slice 1 of stage s
   // is read from LDS while slice 0's MFMAs run; then the wave waits until its own loads of
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     constexpr int AHEAD = decltype(ahead_c)::value;
     const uint8_t* base = smem + (s % C::NS) * C::STAGE;
     read_frag(base, 1, f1);
-    mma(cur0, scur, 0);
+    mma(cur0, scur, Slice0());
     // slice 1's reads one per slice-0 MFMA (after the first); reads beyond the MFMAs go last
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
       read_scales(nb, snxt);
       read_frag(nb, 0, nxt0);
     }
-    mma(f1, scur, 1);
+    mma(f1, scur, Slice1());
     // the next stage's scale words and slice-0 reads one per slice-1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
