@@ -50,6 +50,21 @@ struct MxCfg {
   static constexpr int SMEM = NS * STAGE;
 };
 
+// Word 3 of a raw buffer resource on gfx9-family GPUs (no swizzle, 32-bit data format; the
+// value AMD's composable_kernel uses for these targets).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Direct loads into LDS through a raw buffer resource over [array, array + bytes): 16 (4) bytes
+// per lane from array + voffset + soffset (soffset wave-uniform) to the lane's slot at lds.
+__device__ __forceinline__ void buffer_to_lds16(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
+                                           (lds_ptr_t)lds, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
+                                           (lds_ptr_t)lds, 4, voffset, soffset, 0, 0);
+}
+
 __device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 template <class DT, int BM, int BN>
@@ -77,9 +92,11 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   const int tm = gm0 + in_g % gsz, tn = in_g / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // ---- per-lane DMA sources (16-byte chunks) for this wave's share of a stage
-  const uint8_t* a_src[C::A_PER_WAVE];
-  int a_dst[C::A_PER_WAVE];
+  // ---- per-lane DMA sources (16-byte chunks) for this wave's share of a stage, as 32-bit byte
+  // offsets into buffer resources over the four operand arrays (each under 2 GiB, checked by
+  // the launcher): the stage advance is the instruction's scalar offset, so a load needs no
+  // address arithmetic in the loop, and a resource's range check covers exactly its array.
+  int a_off[C::A_PER_WAVE], a_dst[C::A_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < C::A_PER_WAVE; j++) {
     const int u = wave + C::NWV * j;  // instruction index: 16 rows x 64 bytes
@@ -88,11 +105,10 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const int chunk = phys ^ ((row >> 2) & 3);
     int gr = m0 + row;
     gr = gr < p.B ? gr : p.B - 1;
-    a_src[j] = p.acodes + (int64_t)gr * p.lda + chunk * 16;
+    a_off[j] = gr * p.lda + chunk * 16;
     a_dst[j] = u * 1024;
   }
-  const uint8_t* b_src[C::B_PER_WAVE];
-  int b_dst[C::B_PER_WAVE];
+  int b_off[C::B_PER_WAVE], b_dst[C::B_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < C::B_PER_WAVE; j++) {
     int u = wave + C::NWV * j;
@@ -102,7 +118,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const int chunk = phys ^ ((row >> 2) & 3);
     int gr = n0 + row;
     gr = gr < p.npad ? gr : p.npad - 1;
-    b_src[j] = p.wcodes + mx_code_tile_offset(gr, p.kq) + chunk * 16;  // tiled: + 1024 per stage
+    b_off[j] = (int)mx_code_tile_offset(gr, p.kq) + chunk * 16;  // tiled: + 1024 per stage
     b_dst[j] = C::A_BYTES + u * 1024;  // u >= B_INSTR lands in the padding after B
   }
   // scales (stage-tiled): waves 0-3 load the 64-row groups 0-3 of the A tile, waves 4-7 those of
@@ -111,25 +127,23 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   const int sw = wave & 3;
   int ga = (m0 >> 6) + sw;
   ga = ga < p.ascale_groups ? ga : p.ascale_groups - 1;
-  const uint8_t* sa_src = p.ascales + ((int64_t)ga * p.kq << 8) + lane * 4;
+  const int sa_off = ((ga * p.kq) << 8) + lane * 4;
   int gb = (n0 >> 6) + (64 * sw < BN ? sw : 0);
   gb = gb < (p.npad >> 6) ? gb : (p.npad >> 6) - 1;
-  const uint8_t* sb_src = p.wscales + ((int64_t)gb * p.kq << 8) + lane * 4;
+  const int sb_off = ((gb * p.kq) << 8) + lane * 4;
   const int s_off_a = C::A_BYTES + C::B_PER_WAVE * C::NWV * 1024;
   const int s_off_b = s_off_a + C::SCALE_BYTES;
 
   auto issue = [&](int st) {
     uint8_t* base = smem + (st % C::NS) * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::A_PER_WAVE; j++)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + st * C::SB), (lds_ptr_t)(base + a_dst[j]), 16, 0, 0);
+    for (int j = 0; j < C::A_PER_WAVE; j++) buffer_to_lds16(p.acodes, (int)((int64_t)p.B * p.lda), base + a_dst[j], a_off[j], st * C::SB);
 #pragma unroll
-    for (int j = 0; j < C::B_PER_WAVE; j++)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + (int64_t)st * 1024), (lds_ptr_t)(base + b_dst[j]), 16, 0, 0);
+    for (int j = 0; j < C::B_PER_WAVE; j++) buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * p.kq * 64), base + b_dst[j], b_off[j], st * 1024);
     if (wave < 4)
-      __builtin_amdgcn_global_load_lds((const void*)(sa_src + st * 256), (lds_ptr_t)(base + s_off_a + sw * 256), 4, 0, 0);
+      buffer_to_lds4(p.ascales, (int)((int64_t)p.ascale_groups * p.kq * 256), base + s_off_a + sw * 256, sa_off, st * 256);
     else
-      __builtin_amdgcn_global_load_lds((const void*)(sb_src + st * 256), (lds_ptr_t)(base + s_off_b + sw * 256), 4, 0, 0);
+      buffer_to_lds4(p.wscales, (int)((int64_t)(p.npad >> 6) * p.kq * 256), base + s_off_b + sw * 256, sb_off, st * 256);
   };
 
   v16f acc[C::MT][C::NT];
@@ -430,6 +444,11 @@ static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
 // the shape or dtype is not covered, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
   if (dtype != SVDQ_BF16 || p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
+  // the operand arrays are addressed through buffer resources with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.kq * 64 >= lim ||
+      (int64_t)p.ascale_groups * p.kq * 256 >= lim || (int64_t)(p.npad >> 6) * p.kq * 256 >= lim)
+    return hipErrorNotSupported;
   // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
   // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192). Batches of
   // at most 128 rows take 128-row tiles: half the padded rows' MFMAs and operand bytes.
