@@ -1,13 +1,30 @@
-// Pieces shared by the LDS-ring GEMM kernels: the LDS address space pointer type for
-// direct global->LDS loads, and waits on the vector-memory counter.
+// Pieces shared by the LDS-ring GEMM kernels: the LDS address space pointer type and direct
+// buffer->LDS loads, and waits on the vector-memory counter.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <cstdint>
 
 namespace svdq {
 namespace dev {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs (no swizzle, 32-bit data format; the
+// value AMD's composable_kernel uses for these targets).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Direct loads into LDS through a raw buffer resource over [array, array + bytes): 16 (4) bytes
+// per lane from array + voffset + soffset (soffset wave-uniform) to the lane's slot at lds.
+__device__ __forceinline__ void buffer_to_lds16(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
+                                           (lds_ptr_t)lds, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
+                                           (lds_ptr_t)lds, 4, voffset, soffset, 0, 0);
+}
 
 // s_waitcnt vmcnt(n) for a compile-time n (expcnt and lgkmcnt left at their maxima).
 template <int N>

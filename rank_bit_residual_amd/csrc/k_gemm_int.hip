@@ -87,16 +87,17 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   if ((ntiles & 7) == 0) tid = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
   const int m0 = (tid % tiles_m) * BM, n0 = (tid / tiles_m) * BN;
 
-  // ---- per-lane DMA sources: wave-wide instruction u covers 8 rows x 128 bytes
-  const uint8_t* a_src[A_PER_WAVE];
-  const uint8_t* b_src[B_PER_WAVE];
+  // ---- per-lane DMA sources: wave-wide instruction u covers 8 rows x 128 bytes; 32-bit byte
+  // offsets into buffer resources over the two code arrays (each under 2 GiB, checked by the
+  // launcher), the stage advance being the instruction's scalar offset
+  int a_off[A_PER_WAVE], b_off[B_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < A_PER_WAVE; j++) {
     const int q = (wave + 4 * j) * 64 + lane;
     const int row = q >> 3, chunk = (q & 7) ^ ((row >> 1) & 7);
     int gr = m0 + row;
     gr = gr < p.B ? gr : p.B - 1;
-    a_src[j] = p.acodes + (int64_t)gr * p.lda + chunk * 16;
+    a_off[j] = gr * p.lda + chunk * 16;
   }
 #pragma unroll
   for (int j = 0; j < B_PER_WAVE; j++) {
@@ -104,18 +105,16 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
     const int row = q >> 3, chunk = (q & 7) ^ ((row >> 1) & 7);
     int gr = n0 + row;
     gr = gr < p.npad ? gr : p.npad - 1;
-    b_src[j] = p.wcodes + (int64_t)gr * p.ldw + chunk * 16;
+    b_off[j] = gr * p.ldw + chunk * 16;
   }
+  const int a_bytes = p.B * p.lda, b_bytes = p.npad * p.ldw;
   auto issue = [&](int st) {
     uint8_t* base = smem + (st % NS) * STAGE;
 #pragma unroll
-    for (int j = 0; j < A_PER_WAVE; j++)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + st * SB), (lds_ptr_t)(base + (wave + 4 * j) * 1024),
-                                       16, 0, 0);
+    for (int j = 0; j < A_PER_WAVE; j++) buffer_to_lds16(p.acodes, a_bytes, base + (wave + 4 * j) * 1024, a_off[j], st * SB);
 #pragma unroll
     for (int j = 0; j < B_PER_WAVE; j++)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + st * SB),
-                                       (lds_ptr_t)(base + A_BYTES + (wave + 4 * j) * 1024), 16, 0, 0);
+      buffer_to_lds16(p.wcodes, b_bytes, base + A_BYTES + (wave + 4 * j) * 1024, b_off[j], st * SB);
   };
 
   v16i acc[2][2];
@@ -367,6 +366,9 @@ static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
 // K stages; shorter K falls back to the general kernel.
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
   if (p.kstages < gi::DIST) return hipErrorNotSupported;
+  // the code arrays are addressed through buffer resources with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.ldw >= lim) return hipErrorNotSupported;
   if (bits <= 4) return dtype == SVDQ_BF16 ? launch_int4_t<BF16, true>(p, stream) : launch_int4_t<F32, true>(p, stream);
   return dtype == SVDQ_BF16 ? launch_int4_t<BF16, false>(p, stream) : launch_int4_t<F32, false>(p, stream);
 }

@@ -50,21 +50,6 @@ struct MxCfg {
   static constexpr int SMEM = NS * STAGE;
 };
 
-// Word 3 of a raw buffer resource on gfx9-family GPUs (no swizzle, 32-bit data format; the
-// value AMD's composable_kernel uses for these targets).
-constexpr int kBufferRsrcWord3 = 0x00020000;
-
-// Direct loads into LDS through a raw buffer resource over [array, array + bytes): 16 (4) bytes
-// per lane from array + voffset + soffset (soffset wave-uniform) to the lane's slot at lds.
-__device__ __forceinline__ void buffer_to_lds16(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
-                                           (lds_ptr_t)lds, 16, voffset, soffset, 0, 0);
-}
-__device__ __forceinline__ void buffer_to_lds4(const uint8_t* array, int bytes, uint8_t* lds, int voffset, int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)array, 0, bytes, kBufferRsrcWord3),
-                                           (lds_ptr_t)lds, 4, voffset, soffset, 0, 0);
-}
-
 __device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 template <class DT, int BM, int BN>
