@@ -359,14 +359,19 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   }
 
   // ---- epilogue: one rounding, staged through the (now idle) LDS ring for 16-byte stores. In a
-  // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Neighbouring lanes
-  // swap one value (DPP quad_perm [1,0,3,2]) so that the even lane holds row 8q + 4g + e,
-  // columns (l32, l32+1) and the odd lane row 8q + 4g + e + 1 of the same two columns
-  // (e = 0, 2): one 4-byte LDS write per pair.
+  // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Each lane rounds
+  // rows (r, r+1) of its column into one word (e = 0, 2), neighbouring lanes swap those words
+  // (DPP quad_perm [1,0,3,2]), and one byte permute leaves the even lane row r of columns
+  // (l32, l32+1) and the odd lane row r+1 of the same two columns: one 4-byte LDS write per
+  // pair and no per-pair select.
   static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
   const bool odd = l32 & 1;
+  // perm(neighbour, own): bytes 0-3 are the own word, 4-7 the neighbour's; the even lane takes
+  // (own.lo, neighbour.lo), the odd lane (neighbour.hi, own.hi)
+  const u32 psel = odd ? 0x03020706u : 0x05040100u;
   __syncthreads();
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* wtile = tile + (odd ? BN : 0);
 #pragma unroll
   for (int i = 0; i < C::MT; i++)
 #pragma unroll
@@ -376,12 +381,10 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
       for (int q = 0; q < 4; q++)
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-          const float m0v = acc[i][j][4 * q + e], m1v = acc[i][j][4 * q + e + 1];
-          const float send = odd ? m0v : m1v;
-          const float recv = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-          const u32 w = odd ? pack_bf16x2(recv, m1v) : pack_bf16x2(m0v, recv);
-          const int r = wm * C::TM + 32 * i + 8 * q + 4 * g + e + (odd ? 1 : 0);
-          *reinterpret_cast<u32*>(tile + r * BN + c) = w;
+          const u32 own = pack_bf16x2(acc[i][j][4 * q + e], acc[i][j][4 * q + e + 1]);
+          const u32 nb = (u32)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
+          const int r = wm * C::TM + 32 * i + 8 * q + 4 * g + e;
+          *reinterpret_cast<u32*>(wtile + r * BN + c) = __builtin_amdgcn_perm(nb, own, psel);
         }
     }
   __syncthreads();
