@@ -179,6 +179,34 @@ def test_int_linear_graph_replay_matches_eager():
         assert torch.equal(out, want)
 
 
+def test_int_small_batch_many_calls_same_results():
+    """The INT path (maximum pre-pass, activation kernel, GEMM) keeps no state between calls:
+    1100 back-to-back calls on one workspace alternate two batches of different ranges (so
+    s_x changes every call); each must reproduce its batch's first result bit for bit, and
+    the first results match the oracle."""
+    rng = np.random.default_rng(23)
+    B, M, N = 64, 2048, 384
+    xs = [O.to_dtype(rng.standard_normal((B, M)) * (1 + 3 * k), "bf16") for k in range(2)]
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)), "bf16")
+    from workloads import smoothing_scale
+    s = smoothing_scale(xs[0], w, 0.5)
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(s), 32, 4, "int", keep_factors=True)
+    ws = torch.empty(R.workspace_bytes(B, p), dtype=torch.uint8, device=dev())
+    want = [R.linear(_g(x, "bf16"), p, workspace=ws).clone() for x in xs]
+    for x, y in zip(xs, want):
+        ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "int", 4, "bf16")
+        assert O.rel_fro(_np(y), ref) <= TOL["bf16"]
+    xg = [_g(x, "bf16") for x in xs]
+    outs = torch.empty((100, B, N), dtype=torch.bfloat16, device=dev())
+    for rnd in range(11):
+        outs.fill_(float("nan"))
+        for k in range(100):
+            R.linear(xg[k % 2], p, out=outs[k], workspace=ws)
+        torch.cuda.synchronize()
+        for k in range(100):
+            assert torch.equal(outs[k], want[k % 2]), f"call {100 * rnd + k} differs"
+
+
 @pytest.mark.parametrize("B,M,N", [(4200, 1536, 256), (300, 4096, 200)])
 def test_int_linear_batch_routes(B, M, N):
     """B = 4200: 263 row blocks, no K split, two K steps per wave of the activation kernel;
