@@ -17,6 +17,8 @@
 // operands are requested ahead of the residual codes and multiplied while the codes are still
 // in flight. The partial tiles are summed in LDS in a fixed order, and one wave rounds and
 // stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/svdq.h"
@@ -27,10 +29,14 @@ namespace dev {
 constexpr int DEC_COLS = 32;   // output columns per block
 
 // MT: 16-row tiles of the batch; DEC_WAVES: waves per block, each taking 1/DEC_WAVES of K
-// (eight, two per SIMD, while the registers allow; four with four row tiles)
-template <int MT, int DEC_WAVES>
+// (eight, two per SIMD, while the registers allow; four with four row tiles). DT: the io
+// dtype (x, down, L2, bias and Y): bf16 takes the up-projection on bf16 MFMAs, f32 on f32
+// MFMAs (16x16x4) with no rounding of its operands.
+template <class DT, int MT, int DEC_WAVES>
 __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p) {
-  typedef BF16::T T;
+  typedef typename DT::T T;
+  // up-projection operands of one lane: four consecutive rank entries as stored
+  typedef typename std::conditional<DT::is_bf16, v4s, v4f>::type U4;
   constexpr int DEC_BATCH = MT >= 2 ? 4 : 8;  // K steps per load batch
   __shared__ float red[DEC_WAVES][MT][2][64][4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -77,9 +83,10 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
   };
 
   // ---- up-projection operands. Wave w owns rank columns [16 w + UPW j, +16) for j = 0, 1, ...
-  // (16x16x16 bf16 MFMAs: lane (i, g) holds down[row i][4 g .. 4 g + 3] and L2^T[col i][same]).
+  // (lane (i, g) holds down[row i][4 g .. 4 g + 3] and L2^T[col i][same]; bf16: one 16x16x16
+  // MFMA per tile, f32: four 16x16x4 MFMAs, the e-th taking entries 4 g + e of the lanes).
   // down is either the finished [B][rp] matrix or the sum, in chunk order, of the f32 split-K
-  // partials, rounded once to bf16. Round j = 0 is loaded before the residual codes, so its
+  // partials (rounded once to bf16 for bf16 io). Round j = 0 is loaded before the residual codes, so its
   // requests travel together with them and its MFMAs run while the codes are still in flight.
   constexpr int UPW = 16 * DEC_WAVES;
   constexpr int PF = MT >= 4 ? 2 : 8 / MT;  // split-K partials prefetched per round (the rest are summed after)
@@ -93,17 +100,17 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
     ucol[tt] = col < p.npad ? col : p.npad - 1;
   }
   struct UpOps {
-    v4s b[2];
+    U4 b[2];
     v4f part[MT][PF];  // split-K partials (down_chunks > 1)
-    v4s d[MT];         // finished down entries (down_chunks <= 1)
+    U4 d[MT];          // finished down entries (down_chunks <= 1)
   };
   auto up_load = [&](UpOps& u, int kk) {
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++) u.b[tt] = *reinterpret_cast<const v4s*>(l2t + (int64_t)ucol[tt] * p.rp + kk);
+    for (int tt = 0; tt < 2; tt++) u.b[tt] = *reinterpret_cast<const U4*>(l2t + (int64_t)ucol[tt] * p.rp + kk);
     if (p.down_chunks <= 1) {
 #pragma unroll
       for (int m = 0; m < MT; m++)
-        u.d[m] = *reinterpret_cast<const v4s*>(reinterpret_cast<const T*>(p.down) + (int64_t)urow[m] * p.rp + kk);
+        u.d[m] = *reinterpret_cast<const U4*>(reinterpret_cast<const T*>(p.down) + (int64_t)urow[m] * p.rp + kk);
     } else {
       const int64_t stride = (int64_t)p.B * p.rp;
 #pragma unroll
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
   auto up_mma = [&](const UpOps& u, int kk) {
 #pragma unroll
     for (int m = 0; m < MT; m++) {
-      v4s a;
+      U4 a;
       if (p.down_chunks <= 1) {
         a = u.d[m];
       } else {
@@ -128,11 +135,22 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
         const int64_t stride = (int64_t)p.B * p.rp;
         for (int c = PF; c < p.down_chunks; c++)
           sum += *reinterpret_cast<const v4f*>(p.down_part + c * stride + (int64_t)urow[m] * p.rp + kk);
-        const u32 lo = pack_bf16x2(sum[0], sum[1]), hi = pack_bf16x2(sum[2], sum[3]);
-        a = __builtin_bit_cast(v4s, v2u{lo, hi});
+        if constexpr (DT::is_bf16) {
+          const u32 lo = pack_bf16x2(sum[0], sum[1]), hi = pack_bf16x2(sum[2], sum[3]);
+          a = __builtin_bit_cast(v4s, v2u{lo, hi});
+        } else {
+          a = sum;
+        }
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; tt++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, u.b[tt], acc[m][tt], 0, 0, 0);
+      for (int tt = 0; tt < 2; tt++) {
+        if constexpr (DT::is_bf16) {
+          acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, u.b[tt], acc[m][tt], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], u.b[tt][e], acc[m][tt], 0, 0, 0);
+        }
+      }
     }
   };
   const int kk0 = 16 * wave + 4 * g;  // this lane's first rank column of round 0
@@ -234,12 +252,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
       const int col = n0 + 16 * tt + i;
-      const float bz = bias_at<BF16>(p.bias, col, p.N);
+      const float bz = bias_at<DT>(p.bias, col, p.N);
       if (col >= p.N) continue;
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int row = 16 * m + 4 * g + v;
-        if (row < p.B) __builtin_nontemporal_store(BF16::from_f32(acc[m][tt][v] * al + bz), y + (int64_t)row * p.ldy + col);
+        if (row < p.B) __builtin_nontemporal_store(DT::from_f32(acc[m][tt][v] * al + bz), y + (int64_t)row * p.ldy + col);
       }
     }
 }
@@ -248,15 +266,20 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 
 using namespace dev;
 
-hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream) {
-  if (dtype != SVDQ_BF16 || p.B > 64) return hipErrorNotSupported;
+template <class DT>
+static hipError_t launch_decode_t(const GemmParams& p, hipStream_t stream) {
   const int grid = (p.N + DEC_COLS - 1) / DEC_COLS;
   if (p.B <= 16)
-    return launch_gemm_kernel(k_gemm_decode_mx<1, 8>, dim3(grid), dim3(512), 0, stream, p);
+    return launch_gemm_kernel(k_gemm_decode_mx<DT, 1, 8>, dim3(grid), dim3(512), 0, stream, p);
   else if (p.B <= 32)
-    return launch_gemm_kernel(k_gemm_decode_mx<2, 8>, dim3(grid), dim3(512), 0, stream, p);
+    return launch_gemm_kernel(k_gemm_decode_mx<DT, 2, 8>, dim3(grid), dim3(512), 0, stream, p);
   else
-    return launch_gemm_kernel(k_gemm_decode_mx<4, 4>, dim3(grid), dim3(256), 0, stream, p);
+    return launch_gemm_kernel(k_gemm_decode_mx<DT, 4, 4>, dim3(grid), dim3(256), 0, stream, p);
+}
+
+hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream) {
+  if (p.B > 64) return hipErrorNotSupported;
+  return dtype == SVDQ_BF16 ? launch_decode_t<BF16>(p, stream) : launch_decode_t<F32>(p, stream);
 }
 
 }  // namespace svdq

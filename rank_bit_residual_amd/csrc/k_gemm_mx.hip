@@ -52,6 +52,66 @@ struct MxCfg {
 
 __device__ inline int lds_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
+// Eight f32 values as bf16 high parts RN(v) and low parts RN(v - RN(v)).
+__device__ inline void split_bf16x8(const float* v, v8bf& hi, v8bf& lo) {
+  u32 h[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    h[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+    const float r0 = v[2 * q] - __uint_as_float(h[q] << 16), r1 = v[2 * q + 1] - __uint_as_float(h[q] & 0xFFFF0000u);
+    l[q] = pack_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(v8bf, v4i{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+  lo = __builtin_bit_cast(v8bf, v4i{(int)l[0], (int)l[1], (int)l[2], (int)l[3]});
+}
+
+// f32 output of a BM x BN tile: staged through the idle LDS ring in CH row chunks (a whole f32
+// tile is larger than the ring), each written by the waves whose rows it holds (one 4-byte LDS
+// write per value) and stored as 16-byte streaming stores.
+template <int BM, int BN, int MT, int NT>
+__device__ __forceinline__ void store_f32_tile(const GemmParams& p, const v16f (&acc)[MT][NT], uint8_t* smem, int t,
+                                               int wm, int wn, int l32, int g, int m0, int n0) {
+  typedef MxCfg<BM, BN> C;
+  constexpr int CH = (BM * BN * 4 + C::SMEM - 1) / C::SMEM;
+  static_assert(CH == 1 || CH == 2 || CH == 4, "row chunks must split the four wave rows evenly");
+  constexpr int CR = BM / CH;  // rows per chunk
+  float* tile = reinterpret_cast<float*>(smem);
+  float* y = reinterpret_cast<float*>(p.y);
+  constexpr int CPR = BN / 4;  // 16-byte chunks per tile row
+  const bool vec_ok = (p.ldy % 4 == 0) && (((uintptr_t)p.y & 15) == 0);
+#pragma unroll
+  for (int ch = 0; ch < CH; ch++) {
+    __syncthreads();
+    if (wm / (C::WM / CH) == ch) {
+#pragma unroll
+      for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+#pragma unroll
+          for (int v = 0; v < 16; v++) {
+            const int r = wm * C::TM + 32 * i + 8 * (v / 4) + 4 * g + (v % 4) - ch * CR;
+            tile[r * BN + wn * C::TN + 32 * j + l32] = acc[i][j][v];
+          }
+    }
+    __syncthreads();
+    for (int c = t; c < CR * CPR; c += 64 * C::NWV) {
+      const int r = c / CPR, cc = c - r * CPR;
+      const int row = m0 + ch * CR + r, col = n0 + cc * 4;
+      if (row >= p.B || col >= p.N) continue;
+      const float4 v = *reinterpret_cast<const float4*>(tile + r * BN + cc * 4);
+      float* dst = y + (int64_t)row * p.ldy + col;
+      if (vec_ok && col + 4 <= p.N) {
+        __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(dst));
+      } else {
+        const float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (col + q < p.N) dst[q] = w[q];
+      }
+    }
+  }
+}
+
 template <class DT, int BM, int BN>
 __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   typedef MxCfg<BM, BN> C;
@@ -249,7 +309,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   // they arrive, so they are requested after the stages. Every launch has at least two stages.
   UpOps u0;
   const bool up_direct = p.down_chunks <= 1;
-  if (p.rp > 0 && up_direct) {
+  if (DT::is_bf16 && p.rp > 0 && up_direct) {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -264,13 +324,44 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   static_assert(C::DIST == 2, "two stages issued here");
   issue(0);
   issue(1);
-  if (p.rp > 0) {
-    if (!up_direct) up_load(u0, 0);
-    up_mma(u0);
-    for (int kk = 32; kk < p.rp; kk += 32) {
-      UpOps u;
-      up_load(u, kk);
-      up_mma(u);
+  if constexpr (DT::is_bf16) {
+    if (p.rp > 0) {
+      if (!up_direct) up_load(u0, 0);
+      up_mma(u0);
+      for (int kk = 32; kk < p.rp; kk += 32) {
+        UpOps u;
+        up_load(u, kk);
+        up_mma(u);
+      }
+    }
+  } else {
+    // f32 io: down (finished, or the ordered sum of its split-K partials) and L2^T are split
+    // into bf16 high and low parts, and down L2 = dh lh + dh ll + dl lh on bf16 MFMAs (the
+    // dropped dl ll and the split leave a relative error near 2^-16). Requested after the first
+    // stages, so its waits cover them too.
+    for (int kk = 0; kk < p.rp; kk += 16) {
+      v8bf ah[C::MT], al[C::MT];
+#pragma unroll
+      for (int i = 0; i < C::MT; i++) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = down1_f32(p.down, p.down_part, p.down_chunks, p.B, p.rp, drow[i], kk + 8 * g + e);
+        split_bf16x8(v, ah[i], al[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < C::NT; j++) {
+        const float* src = reinterpret_cast<const float*>(p.l2t) + (int64_t)bcol[j] * p.rp + kk + 8 * g;
+        const float4 l0 = *reinterpret_cast<const float4*>(src), l1 = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        v8bf bh, bl;
+        split_bf16x8(v, bh, bl);
+#pragma unroll
+        for (int i = 0; i < C::MT; i++) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh, acc[i][j], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -364,6 +455,10 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   // (DPP quad_perm [1,0,3,2]), and one byte permute leaves the even lane row r of columns
   // (l32, l32+1) and the odd lane row r+1 of the same two columns: one 4-byte LDS write per
   // pair and no per-pair select.
+  if constexpr (!DT::is_bf16) {
+    store_f32_tile<BM, BN>(p, acc, smem, t, wm, wn, l32, g, m0, n0);
+    return;
+  }
   static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
   const bool odd = l32 & 1;
   // perm(neighbour, own): bytes 0-3 are the own word, 4-7 the neighbour's; the even lane takes
@@ -414,24 +509,29 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
 
 using namespace dev;
 
-template <int BM, int BN>
-static hipError_t launch_mx_t(const GemmParams& p, hipStream_t stream) {
+template <class DT, int BM, int BN>
+static hipError_t launch_mx_dt(const GemmParams& p, hipStream_t stream) {
   typedef MxCfg<BM, BN> C;
   const int tiles = ((p.B + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx<BF16, BM, BN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx<DT, BM, BN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  return launch_gemm_kernel(k_gemm_mx<BF16, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
+  return launch_gemm_kernel(k_gemm_mx<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
-// MXFP4 path for bf16 inputs above decode batches (B > 64); returns hipErrorNotSupported when
-// the shape or dtype is not covered, so the caller falls back to the general kernel.
+template <int BM, int BN>
+static hipError_t launch_mx_t(const GemmParams& p, int dtype, hipStream_t stream) {
+  return dtype == SVDQ_BF16 ? launch_mx_dt<BF16, BM, BN>(p, stream) : launch_mx_dt<F32, BM, BN>(p, stream);
+}
+
+// MXFP4 path above decode batches (B > 64), bf16 or f32 io; returns hipErrorNotSupported when
+// the shape is not covered, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
-  if (dtype != SVDQ_BF16 || p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
+  if (p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
   // the operand arrays are addressed through buffer resources with 32-bit offsets
   const int64_t lim = (int64_t)1 << 31;
   if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.kq * 64 >= lim ||
@@ -440,11 +540,12 @@ hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stre
   // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
   // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192). Batches of
   // at most 128 rows take 128-row tiles: half the padded rows' MFMAs and operand bytes.
-  if (p.B <= 128) return p.N % 256 != 0 && p.N % 192 == 0 ? launch_mx_t<128, 192>(p, stream) : launch_mx_t<128, 256>(p, stream);
+  if (p.B <= 128)
+    return p.N % 256 != 0 && p.N % 192 == 0 ? launch_mx_t<128, 192>(p, dtype, stream) : launch_mx_t<128, 256>(p, dtype, stream);
   const int tiles_m = (p.B + 255) / 256;
-  if (p.N % 256 == 0 && tiles_m * (p.N / 256) >= 512) return launch_mx_t<256, 256>(p, stream);
-  if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, stream);
-  return launch_mx_t<256, 256>(p, stream);
+  if (p.N % 256 == 0 && tiles_m * (p.N / 256) >= 512) return launch_mx_t<256, 256>(p, dtype, stream);
+  if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, dtype, stream);
+  return launch_mx_t<256, 256>(p, dtype, stream);
 }
 
 }  // namespace svdq

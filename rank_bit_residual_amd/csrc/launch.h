@@ -101,7 +101,7 @@ hipError_t launch_calibrate(const void* x, int B, int M, int64_t ldx, const void
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
 // Per-tensor INT, bits <= 4: 64x64 tiles, K split over the waves of a block (kstages = Kp/256).
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream);
-// MXFP4, bf16, B <= 64: K split over waves, weights streamed straight into registers.
+// MXFP4, B <= 64 (bf16 or f32 io): K split over waves, weights streamed straight into registers.
 hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream);
 
 // Ceiling probes (k_ceiling.hip): kind 0 FP4 MFMA loop, 1 INT8 MFMA loop (arg = iterations),

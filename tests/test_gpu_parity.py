@@ -276,11 +276,11 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
     """The residual GEMM kernel (and MXFP4 tile) svdq_linear launches for a shape: the launch
     rules of the library, restated so that each exact case below names the kernel it aims at."""
     kp = -(-M // 256) * 256
-    if fmt == "mx" and dtype == "bf16" and B <= 64:
+    if fmt == "mx" and B <= 64:
         return "decode"
-    if fmt == "mx" and dtype == "bf16" and B <= 128:
+    if fmt == "mx" and B <= 128:
         return "mx128x192" if N % 256 != 0 and N % 192 == 0 else "mx128x256"
-    if fmt == "mx" and dtype == "bf16":
+    if fmt == "mx":
         tiles_m = -(-B // 256)
         if N % 256 == 0 and tiles_m * (N // 256) >= 512:
             return "mx256x256"
@@ -342,13 +342,16 @@ def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
     (17, 1280, 200, "decode"),       # decode kernel, two row tiles (the second with one live row)
     (40, 768, 96, "decode"),         # decode kernel, four row tiles and four waves
 ])
-def test_mx_kernel_exact_special_case(B, M, N, route):
-    """Plain (not two-level) MXFP4 exact case through each MXFP4 kernel and tile choice."""
-    assert _gemm_route(B, M, N, "mx", 4, "bf16") == route
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mx_kernel_exact_special_case(B, M, N, route, dtype):
+    """Plain (not two-level) MXFP4 exact case through each MXFP4 kernel and tile choice, with
+    bf16 io (one rounding of the exact product) and f32 io (the exact product itself; the f32
+    tile leaves the kernel in row chunks)."""
+    assert _gemm_route(B, M, N, "mx", 4, dtype) == route
     x, w = _e2m1_exact_operands(np.random.default_rng(B + N), B, M, N)
-    p = R.prepare(_g(w, "bf16"), torch.ones(M), 0, 4, "mx")
-    y = R.linear(_g(x, "bf16"), p)
-    want = O.to_dtype(x @ w, "bf16")
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, 4, "mx")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x @ w, dtype)
     got = _np(y)
     bad = np.argwhere(_bits(got) != _bits(want))
     assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
@@ -573,6 +576,29 @@ def test_int4_gemm_shapes(B, M, N, rank, dtype):
 
 
 # ----------------------------------------------------------------------------- decode-batch MXFP4 kernel
+@pytest.mark.parametrize("B,M,N,rank", [
+    (16, 8192, 1024, 128),  # decode kernel: split-K partials of down, two up-projection rounds
+    (40, 3072, 200, 160),   # decode kernel, four row tiles and waves, three up-projection rounds
+    (100, 1024, 576, 64),   # 128-row tiles, N a multiple of 192
+    (300, 768, 1000, 32),   # 256 x 256 tiles, ragged B and N
+    (520, 1536, 768, 96),   # 256 x 192 tiles, three 32-wide up-projection steps
+])
+def test_mx_f32_io_shapes(B, M, N, rank):
+    """MXFP4 with float32 io through the MXFP4 kernels: the up-projection takes f32 down and
+    L2 split into bf16 high and low parts (three bf16 products, relative error near 2^-16).
+    Measured against the oracle: 3e-7 to 5e-6; the bound is 1e-4, far inside the float32
+    tolerance, so a plain bf16 up-projection (~3e-3) would fail it."""
+    rng = np.random.default_rng(B + N + rank)
+    x = O.to_dtype(rng.standard_t(3, (B, M)), "f32")
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 3)) @ rng.standard_normal((3, N)), "f32")
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.25)
+    p = R.prepare(_g(w, "f32"), torch.from_numpy(s), rank, 4, "mx", keep_factors=True)
+    y = R.linear(_g(x, "f32"), p)
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "mx", 4, "f32")
+    assert O.rel_fro(_np(y), ref) <= 1e-4
+
+
 @pytest.mark.parametrize("B,M,N,rank", [
     (1, 9216, 1000, 32),    # single row; each of the 8 waves gets 9 K stages (one batch of 8 + a tail)
     (17, 2048, 520, 16),    # two 16-row tiles, the second with one live row
