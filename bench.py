@@ -41,10 +41,9 @@ def gemm_kernel(wl, B):
         return "k_gemm_decode_mx", os.path.join(CSRC, "k_gemm_decode.hip")
     if wl.fmt == "mx" and wl.dtype == "bf16" and B > 64:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
-    kp = -(-wl.M // 256) * 256
-    # the INT kernel keeps 6 stages in flight: 256 nibble codes (<= 4 bits) or 128 int8 codes each
-    if wl.fmt == "int" and (kp // 256 if wl.bits <= 4 else kp // 128) >= 6:
+    if wl.fmt == "int":
         return "k_gemm_int4", os.path.join(CSRC, "k_gemm_int.hip")
+    # the MXFP4 kernels cover every shape of these workloads (arrays under 2 GiB)
     return "k_gemm", os.path.join(CSRC, "k_gemm.hip")
 
 

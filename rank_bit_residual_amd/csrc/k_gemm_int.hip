@@ -205,40 +205,68 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   };
   typedef std::integral_constant<int, DIST - 1> Steady;
 
-#pragma unroll
-  for (int s = 0; s < DIST; s++)
-    if (s < nst) issue(s);
-  wait_vmcnt<LOADS_PER_STAGE * (DIST - 1)>();  // nst >= DIST (checked by the launcher)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
   Ops oa, ob;
-  read_stage(0, oa);
-  // steady state, unrolled by two so that the operands alternate between oa and ob
-  int s = 0;
-  for (; s + 1 < nst - DIST; s += 2) {
-    issue(s + DIST);
-    stage(s, oa, ob, Steady());
-    issue(s + 1 + DIST);
-    stage(s + 1, ob, oa, Steady());
-  }
-  // the rest: at most one more steady stage, then the last DIST stages (stage nst-DIST+d has
-  // DIST-2-d stages issued after the next one; the last has none to read ahead)
-  auto drain = [&](Ops& x, Ops& y) {
-    StaticFor<0, DIST>::run([&](auto dc) {
-      constexpr int d = decltype(dc)::value;
-      typedef std::integral_constant<int, DIST - 2 - d> Ahead;
-      if constexpr (d & 1)
-        stage(nst - DIST + d, y, x, Ahead());
-      else
-        stage(nst - DIST + d, x, y, Ahead());
-    });
-  };
-  if (s < nst - DIST) {
-    issue(s + DIST);
-    stage(s, oa, ob, Steady());
-    drain(ob, oa);
+  if (nst >= DIST) {
+#pragma unroll
+    for (int s = 0; s < DIST; s++) issue(s);
+    wait_vmcnt<LOADS_PER_STAGE * (DIST - 1)>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_stage(0, oa);
+    // steady state, unrolled by two so that the operands alternate between oa and ob
+    int s = 0;
+    for (; s + 1 < nst - DIST; s += 2) {
+      issue(s + DIST);
+      stage(s, oa, ob, Steady());
+      issue(s + 1 + DIST);
+      stage(s + 1, ob, oa, Steady());
+    }
+    // the rest: at most one more steady stage, then the last DIST stages (stage nst-DIST+d has
+    // DIST-2-d stages issued after the next one; the last has none to read ahead)
+    auto drain = [&](Ops& x, Ops& y) {
+      StaticFor<0, DIST>::run([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        typedef std::integral_constant<int, DIST - 2 - d> Ahead;
+        if constexpr (d & 1)
+          stage(nst - DIST + d, y, x, Ahead());
+        else
+          stage(nst - DIST + d, x, y, Ahead());
+      });
+    };
+    if (s < nst - DIST) {
+      issue(s + DIST);
+      stage(s, oa, ob, Steady());
+      drain(ob, oa);
+    } else {
+      drain(oa, ob);
+    }
   } else {
-    drain(oa, ob);
+    // K shorter than DIST stages: all nst stages are issued at once, then consumed in order
+    // (stage d has nst-2-d stages issued after the next one)
+    auto run_short = [&](auto nc) {
+      constexpr int NST = decltype(nc)::value;
+      StaticFor<0, NST>::run([&](auto sc) { issue(decltype(sc)::value); });
+      wait_vmcnt<LOADS_PER_STAGE * (NST - 1)>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      read_stage(0, oa);
+      StaticFor<0, NST>::run([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        typedef std::integral_constant<int, NST - 2 - d> Ahead;
+        if constexpr (d & 1)
+          stage(d, ob, oa, Ahead());
+        else
+          stage(d, oa, ob, Ahead());
+      });
+    };
+    static_assert(DIST == 6, "short runs below cover 1 .. DIST - 1 stages");
+    switch (nst) {
+      case 1: run_short(std::integral_constant<int, 1>()); break;
+      case 2: run_short(std::integral_constant<int, 2>()); break;
+      case 3: run_short(std::integral_constant<int, 3>()); break;
+      case 4: run_short(std::integral_constant<int, 4>()); break;
+      default: run_short(std::integral_constant<int, 5>()); break;
+    }
   }
 
   // ---- epilogue operands of this wave's quadrant q = (qi, qj), loaded before the exchange so
@@ -365,7 +393,7 @@ static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
 // Per-tensor INT: nibble codes (at most 4 bits) or int8 codes (5-8 bits), with at least DIST
 // K stages; shorter K falls back to the general kernel.
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
-  if (p.kstages < gi::DIST) return hipErrorNotSupported;
+  if (p.kstages < 1) return hipErrorNotSupported;
   // the code arrays are addressed through buffer resources with 32-bit offsets
   const int64_t lim = (int64_t)1 << 31;
   if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.ldw >= lim) return hipErrorNotSupported;

@@ -99,7 +99,8 @@ hipError_t launch_calibrate(const void* x, int B, int M, int64_t ldx, const void
                             double alpha, float* part, float* scale, hipStream_t stream);
 // Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
-// Per-tensor INT, bits <= 4: 64x64 tiles, K split over the waves of a block (kstages = Kp/256).
+// Per-tensor INT: 64x64 tiles, K split over the waves of a block (kstages = Kp/256 for nibble
+// codes, Kp/128 for int8 codes; any K).
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream);
 // MXFP4, B <= 64 (bf16 or f32 io): K split over waves, weights streamed straight into registers.
 hipError_t launch_gemm_mx_decode(const GemmParams& p, int dtype, hipStream_t stream);

@@ -8,11 +8,11 @@ import bench
 from workloads import WORKLOADS
 
 
-@pytest.mark.parametrize("cid,kernel", [(1, "k_gemm"), (2, "k_gemm_int4"), (3, "k_gemm_mx"), (4, "k_gemm_mx"),
+@pytest.mark.parametrize("cid,kernel", [(1, "k_gemm_int4"), (2, "k_gemm_int4"), (3, "k_gemm_mx"), (4, "k_gemm_mx"),
                                         (5, "k_gemm_decode_mx")])
 def test_gemm_kernel_routing(cid, kernel):
-    """Workload 1 (K = 64) is below the INT4 kernel's six stages of 256 codes, so the library
-    runs the general kernel there."""
+    """Workload 1 (K = 64: one stage of 256 codes, fewer than the six the INT kernel keeps in
+    flight) takes the INT kernel's short-K path."""
     wl = WORKLOADS[cid]
     assert bench.gemm_kernel(wl, wl.B)[0] == kernel
 

@@ -275,7 +275,6 @@ def test_mx_exact_special_case(dtype):
 def _gemm_route(B, M, N, fmt, bits, dtype):
     """The residual GEMM kernel (and MXFP4 tile) svdq_linear launches for a shape: the launch
     rules of the library, restated so that each exact case below names the kernel it aims at."""
-    kp = -(-M // 256) * 256
     if fmt == "mx" and B <= 64:
         return "decode"
     if fmt == "mx" and B <= 128:
@@ -285,9 +284,7 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
         if N % 256 == 0 and tiles_m * (N // 256) >= 512:
             return "mx256x256"
         return "mx256x192" if N % 192 == 0 else "mx256x256"
-    if fmt == "int" and (kp // 256 if bits <= 4 else kp // 128) >= 6:
-        return "int4" if bits <= 4 else "int8"
-    return "generic"
+    return "int4" if bits <= 4 else "int8"
 
 
 def _e2m1_exact_operands(rng, B, M, N):
@@ -310,12 +307,16 @@ def _e2m1_exact_operands(rng, B, M, N):
     (130, 768, 200, 8, "bf16"),     # int8 codes: exactly 6 stages of 128 codes, ragged B and N
     (64, 2048, 328, 6, "f32"),      # int8 codes, 16 stages, float32 io
     (300, 896, 136, 5, "bf16"),     # int8 codes, 7 stages (one odd steady iteration)
+    (40, 320, 300, 4, "bf16"),      # 2 stages: fewer than the 6 kept in flight, all issued at once
+    (70, 200, 96, 3, "f32"),        # 1 stage (K = 200 padded to 256), float32 io
+    (130, 1280, 200, 4, "bf16"),    # 5 stages, the longest short run
+    (33, 384, 72, 8, "f32"),        # int8 codes: 4 stages of 128 codes
 ])
 def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
-    """Rank 0, unit scale, integer x and W with max |.| = qmax through the INT kernel (K of at
-    least six stages of 256 nibble codes or 128 int8 codes): s_x = s_R = 1 and Y = x @ W bit for
-    bit. |Y| <= qmax^2 K < 2^24, so the float32 result is exact and the bf16 one is its single
-    rounding."""
+    """Rank 0, unit scale, integer x and W with max |.| = qmax through the INT kernel (K from
+    one stage of 256 nibble codes or 128 int8 codes up, both sides of the six it keeps in
+    flight): s_x = s_R = 1 and Y = x @ W bit for bit. |Y| <= qmax^2 K < 2^24, so the float32
+    result is exact and the bf16 one is its single rounding."""
     q = 2 ** (bits - 1) - 1
     assert q * q * M < 2 ** 24
     assert _gemm_route(B, M, N, "int", bits, dtype) == ("int4" if bits <= 4 else "int8")
@@ -681,7 +682,7 @@ def test_toy_experiment_through_library():
     (40, 2048, 300, "int", "bf16"),   # INT4 kernel
     (512, 512, 576, "mx", "bf16"),    # large-batch MXFP4 kernel (256 x 192 tiles)
     (16, 1024, 200, "mx", "bf16"),    # decode MXFP4 kernel
-    (48, 320, 130, "int", "f32"),     # generic kernel
+    (48, 320, 130, "int", "f32"),     # INT kernel, short K (two stages)
 ])
 def test_linear_bias_matches_oracle(B, M, N, fmt, dtype):
     rng = np.random.default_rng(B + N)
