@@ -30,8 +30,10 @@ LaunchPlan make_plan(const Dims& d, int64_t B) {
   p.k_chunk_len = (int)round_up(ceil_div(d.Kp, chunks), 128);
   p.k_chunks = (int)ceil_div(d.Kp, p.k_chunk_len);
   p.amax_cols = (int)ceil_div(d.M, 2048);
-  // 8 rows per block, fewer (down to 1) while that leaves under 256 blocks
-  const int64_t amax_rpb = std::max<int64_t>(1, std::min<int64_t>(8, B * p.amax_cols / 256));
+  // 8 rows per block, fewer (down to 1) while that leaves under 256 blocks, more when that
+  // would give over 4096 partial maxima (every wave of the activation kernel reduces them all)
+  int64_t amax_rpb = std::max<int64_t>(1, std::min<int64_t>(8, B * p.amax_cols / 256));
+  amax_rpb = std::max<int64_t>(amax_rpb, ceil_div(B * p.amax_cols, 4096));
   p.amax_rows = (int)std::min<int64_t>(65535, std::max<int64_t>(1, ceil_div(B, amax_rpb)));
   p.amax_blocks = p.amax_cols * p.amax_rows;
   return p;

@@ -677,6 +677,33 @@ def test_toy_experiment_through_library():
         assert np.allclose(a[:8], b[:8], rtol=1e-5, atol=1e-6 * b[0])
 
 
+# ----------------------------------------------------------------------------- operand arrays past 2 GiB
+@pytest.mark.parametrize("fmt", ["int", "mx"])
+def test_activation_codes_past_2gib_take_the_generic_kernel(fmt):
+    """262144 x 16384 bf16 activations (8 GiB) give a 2 GiB activation-code array, past the
+    32-bit buffer offsets of the INT and MXFP4 kernels, so the residual GEMM runs on the
+    generic kernel (64-bit addressing). Unit smoothing and |x| <= 4 except one planted 8 in
+    a sampled row, so the INT per-tensor maximum of the sample is the tensor's; sampled rows
+    at the start, middle and end are compared with the oracle."""
+    B, M, N, rank = 262144, 16384, 64, 16
+    torch.manual_seed(5)
+    xg = torch.randn((B, M), dtype=torch.bfloat16, device=dev()).clamp_(-4, 4)
+    rows = np.array([0, 1, 77, B // 2, B // 2 + 1, B - 2, B - 1])
+    xg[B // 2, 1234] = 8.0
+    rng = np.random.default_rng(6)
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 2)) @ rng.standard_normal((2, N)), "bf16")
+    s = np.ones(M, np.float32)
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(s), rank, 4, fmt, keep_factors=True)
+    y = R.linear(xg, p)
+    torch.cuda.synchronize()
+    got = _np(y[torch.from_numpy(rows).to(dev())])
+    xs = _np(xg[torch.from_numpy(rows).to(dev())])
+    del xg, y
+    torch.cuda.empty_cache()
+    ref = O.forward_ref(xs, s, _np(p.left), _np(p.right), _np(p.residual), fmt, 4, "bf16")
+    assert O.rel_fro(got, ref) <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------- output bias
 @pytest.mark.parametrize("B,M,N,fmt,dtype", [
     (40, 2048, 300, "int", "bf16"),   # INT4 kernel
