@@ -20,6 +20,7 @@
 // The prepared weight codes are tiled 16 columns x 128 codes per 1 KB, so each wave-wide load
 // of a B stage reads one contiguous kilobyte (the activation codes are row-major: 16 rows x 64
 // bytes per load).
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -523,6 +524,25 @@ static hipError_t launch_mx_dt(const GemmParams& p, hipStream_t stream) {
   return launch_gemm_kernel(k_gemm_mx<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
+// Compute units of the current device (looked up once per device; 256 if the query fails).
+static int64_t device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int BM, int BN>
 static hipError_t launch_mx_t(const GemmParams& p, int dtype, hipStream_t stream) {
   return dtype == SVDQ_BF16 ? launch_mx_dt<BF16, BM, BN>(p, stream) : launch_mx_dt<F32, BM, BN>(p, stream);
@@ -537,15 +557,30 @@ hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stre
   if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.kq * 64 >= lim ||
       (int64_t)p.ascale_groups * p.kq * 256 >= lim || (int64_t)(p.npad >> 6) * p.kq * 256 >= lim)
     return hipErrorNotSupported;
-  // 256 x 256 tiles move the least operand data per flop; 256 x 192 fills the chip better when
-  // there are few tiles (e.g. N = 3072 gives 12 column tiles of 256 but 16 of 192). Batches of
-  // at most 128 rows take 128-row tiles: half the padded rows' MFMAs and operand bytes.
-  if (p.B <= 128)
-    return p.N % 256 != 0 && p.N % 192 == 0 ? launch_mx_t<128, 192>(p, dtype, stream) : launch_mx_t<128, 256>(p, dtype, stream);
-  const int tiles_m = (p.B + 255) / 256;
-  if (p.N % 256 == 0 && tiles_m * (p.N / 256) >= 512) return launch_mx_t<256, 256>(p, dtype, stream);
-  if (p.N % 192 == 0) return launch_mx_t<256, 192>(p, dtype, stream);
-  return launch_mx_t<256, 256>(p, dtype, stream);
+  // Tile shape: the candidate with the least estimated time, rounds of the chip x time per
+  // round. A round (every compute unit on one tile) was measured at K = 3072 to take about
+  // 10 us + 0.3 ns per output element of the tile: 128x192 17.4 us, 128x256 19.8, 256x192 24.7,
+  // 256x256 29.7. So the fewest rounds win first, then the smallest tile (more compute units
+  // busy); 192-wide tiles only when N is a multiple of 192. At 4096 rows this picks 256x256 for
+  // N = 12288 and 256x192 for N = 3072; at 512 rows or fewer, 128-row tiles.
+  const int64_t cus = device_cus();
+  int best = -1;
+  double best_t = 0;
+  const int cand[4][2] = {{128, 192}, {128, 256}, {256, 192}, {256, 256}};
+  for (int c = 0; c < 4; c++) {
+    const int bm = cand[c][0], bn = cand[c][1];
+    if (bn == 192 && p.N % 192 != 0) continue;
+    const int64_t tiles = ((int64_t)(p.B + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const double t = (double)rounds * (10.0 + 0.3e-3 * bm * bn);
+    if (best < 0 || t < best_t) best = c, best_t = t;
+  }
+  switch (best) {
+    case 0: return launch_mx_t<128, 192>(p, dtype, stream);
+    case 1: return launch_mx_t<128, 256>(p, dtype, stream);
+    case 2: return launch_mx_t<256, 192>(p, dtype, stream);
+    default: return launch_mx_t<256, 256>(p, dtype, stream);
+  }
 }
 
 }  // namespace svdq

@@ -277,13 +277,18 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
     rules of the library, restated so that each exact case below names the kernel it aims at."""
     if fmt == "mx" and B <= 64:
         return "decode"
-    if fmt == "mx" and B <= 128:
-        return "mx128x192" if N % 256 != 0 and N % 192 == 0 else "mx128x256"
     if fmt == "mx":
-        tiles_m = -(-B // 256)
-        if N % 256 == 0 and tiles_m * (N // 256) >= 512:
-            return "mx256x256"
-        return "mx256x192" if N % 192 == 0 else "mx256x256"
+        # fewest rounds of 256 compute units x per-round time 10 us + 0.3 ns per tile element;
+        # 192-wide tiles only when N % 192 == 0; the first of equal estimates wins
+        best = None
+        for bm, bn in ((128, 192), (128, 256), (256, 192), (256, 256)):
+            if bn == 192 and N % 192:
+                continue
+            rounds = -(-(-(-B // bm) * -(-N // bn)) // 256)
+            t = rounds * (10.0 + 0.3e-3 * bm * bn)
+            if best is None or t < best[0]:
+                best = (t, f"mx{bm}x{bn}")
+        return best[1]
     return "int4" if bits <= 4 else "int8"
 
 
@@ -333,8 +338,9 @@ def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
 
 
 @pytest.mark.parametrize("B,M,N,route", [
-    (520, 512, 576, "mx256x192"),    # the attention-projection tile (N a multiple of 192), ragged B
-    (200, 512, 392, "mx256x256"),    # 128 < B < 256: one 256-row tile with 56 padded rows
+    (4096, 256, 3072, "mx256x192"),  # the attention-projection tile: 256 tiles, one round
+    (520, 512, 576, "mx128x192"),    # 15 tiles of 128 x 192, ragged B
+    (200, 512, 392, "mx128x256"),    # two 128-row tiles, the second with 72 live rows, ragged N
     (100, 512, 576, "mx128x192"),    # B <= 128: 128-row tiles, N a multiple of 192
     (128, 768, 512, "mx128x256"),    # one full 128-row tile
     (65, 256, 300, "mx128x256"),     # one live row past the decode range, ragged N
