@@ -9,6 +9,9 @@
 // item 3 (Y = (X^ L1) L2 + Q(X^) Q(R)); "flashinfer.gemm.svdquant_linear" (the residual GEMM
 // with the low-rank up-projection fused into its epilogue is prior art for this split).
 //
+// It serves the shapes the specialised kernels decline: operand arrays past 2 GiB, which they
+// address through buffer resources with 32-bit offsets (this kernel uses 64-bit addresses).
+//
 // Tiling: a 128x128 output tile per 256-thread block (2x2 waves of 64x64, each 2x2 MFMA
 // tiles of 32x32). K advances in stages of 128 bytes per row (256 FP4 / INT4 codes or 128
 // int8 codes), double-buffered in LDS; rows are stored as eight 16-byte chunks at position

@@ -16,7 +16,8 @@
 //
 // Structure: a 64 x 64 output tile per 256-thread block, so that mid-size batches still give
 // hundreds of blocks. K advances in stages of 256 codes (128 bytes per row) that land in a
-// ring of LDS buffers through direct global->LDS loads, two stages ahead. Within a stage the
+// ring of LDS buffers through direct global->LDS loads, six stages ahead (all of them when K
+// has fewer stages). Within a stage the
 // four waves split K: wave w takes the 16-byte chunks 2w and 2w+1 (two 32-code MFMA steps)
 // for the whole 64 x 64 tile, which keeps the nibble unpacking below the MFMA time. After
 // the K loop the four int32 partial tiles are summed through LDS (exact), and each wave
@@ -390,8 +391,8 @@ static hipError_t launch_int4_t(const GemmParams& p, hipStream_t stream) {
   return launch_gemm_kernel(k_gemm_int4<DT, NIB>, dim3(tiles), dim3(256), gi::SMEM, stream, p);
 }
 
-// Per-tensor INT: nibble codes (at most 4 bits) or int8 codes (5-8 bits), with at least DIST
-// K stages; shorter K falls back to the general kernel.
+// Per-tensor INT: nibble codes (at most 4 bits) or int8 codes (5-8 bits), any K; operand
+// arrays past 2 GiB fall back to the general kernel.
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream) {
   if (p.kstages < 1) return hipErrorNotSupported;
   // the code arrays are addressed through buffer resources with 32-bit offsets

@@ -549,7 +549,7 @@ static hipError_t launch_mx_t(const GemmParams& p, int dtype, hipStream_t stream
 }
 
 // MXFP4 path above decode batches (B > 64), bf16 or f32 io; returns hipErrorNotSupported when
-// the shape is not covered, so the caller falls back to the general kernel.
+// an operand array is past 2 GiB, so the caller falls back to the general kernel.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
   if (p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
   // the operand arrays are addressed through buffer resources with 32-bit offsets
