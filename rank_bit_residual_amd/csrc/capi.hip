@@ -386,7 +386,8 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   }
   if (fmt == SVDQ_FMT_INT) {
     g.kstages = (int)(d.code_row_bytes() / 128);  // 128-byte stages (256 codes)
-    ge = launch_gemm_int4(g, bits, dtype, s);
+    ge = launch_gemm_int_big(g, bits, dtype, s);
+    if (ge == hipErrorNotSupported) ge = launch_gemm_int4(g, bits, dtype, s);
   }
   if (ge == hipErrorNotSupported) ge = launch_gemm(g, fmt, bits, dtype, s);
   tm.gemm_end(ge);

@@ -113,11 +113,19 @@ __device__ __forceinline__ void store_f32_tile(const GemmParams& p, const v16f (
   }
 }
 
-template <class DT, int BM, int BN>
-__global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
+// One BM x BN tile of the residual GEMM. INTC = false: MXFP4 (FP4 codes with E8M0 scales,
+// weight codes tiled 16 columns x 128 codes per 1 KB). INTC = true: per-tensor INT with nibble
+// codes (both operands row-major, K-contiguous; no per-block scales): each FP4 MFMA's slot
+// becomes two int8 MFMAs on the odd and even codes (a nibble in the high half of a byte reads
+// as 16 times the code), accumulated exactly in int32 and dequantised by s_x s_R / 256 after
+// the K loop, where the up-projection follows.
+template <class DT, int BM, int BN, bool INTC>
+__device__ __forceinline__ void gemm_big(const GemmParams& p) {
   typedef MxCfg<BM, BN> C;
   typedef typename DT::T T;
   extern __shared__ __align__(1024) uint8_t smem[];
+  // per-wave DMA loads of a stage (INT has no scale words)
+  constexpr int LPS = C::A_PER_WAVE + C::B_PER_WAVE + (INTC ? 0 : 1);
 
   // the wave index is uniform across the wave: kept in a scalar register, so that the LDS
   // destinations of the DMA loads are computed on the scalar unit
@@ -164,7 +172,8 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     const int chunk = phys ^ ((row >> 2) & 3);
     int gr = n0 + row;
     gr = gr < p.npad ? gr : p.npad - 1;
-    b_off[j] = (int)mx_code_tile_offset(gr, p.kq) + chunk * 16;  // tiled: + 1024 per stage
+    // MX: tiled, + 1024 per stage; INT: row-major like A, + 64 per stage
+    b_off[j] = INTC ? gr * (int)p.ldw + chunk * 16 : (int)mx_code_tile_offset(gr, p.kq) + chunk * 16;
     b_dst[j] = C::A_BYTES + u * 1024;  // u >= B_INSTR lands in the padding after B
   }
   // scales (stage-tiled): waves 0-3 load the 64-row groups 0-3 of the A tile, waves 4-7 those of
@@ -185,20 +194,24 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < C::A_PER_WAVE; j++) buffer_to_lds16(p.acodes, (int)((int64_t)p.B * p.lda), base + a_dst[j], a_off[j], st * C::SB);
 #pragma unroll
-    for (int j = 0; j < C::B_PER_WAVE; j++) buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * p.kq * 64), base + b_dst[j], b_off[j], st * 1024);
-    if (wave < 4)
-      buffer_to_lds4(p.ascales, (int)((int64_t)p.ascale_groups * p.kq * 256), base + s_off_a + sw * 256, sa_off, st * 256);
-    else
-      buffer_to_lds4(p.wscales, (int)((int64_t)(p.npad >> 6) * p.kq * 256), base + s_off_b + sw * 256, sb_off, st * 256);
+    for (int j = 0; j < C::B_PER_WAVE; j++)
+      buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * p.kq * 64), base + b_dst[j], b_off[j], st * (INTC ? C::SB : 1024));
+    if constexpr (!INTC) {
+      if (wave < 4)
+        buffer_to_lds4(p.ascales, (int)((int64_t)p.ascale_groups * p.kq * 256), base + s_off_a + sw * 256, sa_off, st * 256);
+      else
+        buffer_to_lds4(p.wscales, (int)((int64_t)(p.npad >> 6) * p.kq * 256), base + s_off_b + sw * 256, sb_off, st * 256);
+    }
   };
 
-  v16f acc[C::MT][C::NT];
+  typedef typename std::conditional<INTC, v16i, v16f>::type Acc;
+  Acc acc[C::MT][C::NT];
 #pragma unroll
   for (int i = 0; i < C::MT; i++)
 #pragma unroll
     for (int j = 0; j < C::NT; j++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0;
 
   // Operand fragment of one 64-code K slice: A rows and B columns of this wave's tile read
   // from the LDS stage buffer.
@@ -236,6 +249,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   // byte 2 ks of it (the instruction's scale byte select).
   const int gsh = 8 * g;
   auto read_scales = [&](const uint8_t* base, Scales& sc) {
+    if constexpr (INTC) return;
 #pragma unroll
     for (int i = 0; i < C::MT; i++) sc.a[i] = *reinterpret_cast<const u32*>(base + sa_lane + 128 * i) >> gsh;
 #pragma unroll
@@ -243,12 +257,38 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   };
   auto mma = [&](const Frag& f, const Scales& sc, auto ks_c) {
     constexpr int KS = decltype(ks_c)::value;
+    if constexpr (INTC) {
+      // lane (l32, g) holds 32 nibble codes of K block 2 KS + g: odd codes (w & 0xF0F0F0F0)
+      // and even codes ((w << 4) & 0xF0F0F0F0) as int8 times 16, one 32x32x32 MFMA each
+      const v4i m = {(int)0xF0F0F0F0, (int)0xF0F0F0F0, (int)0xF0F0F0F0, (int)0xF0F0F0F0};
+      v4i ah[C::MT], al[C::MT], bh[C::NT], bl[C::NT];
 #pragma unroll
-    for (int i = 0; i < C::MT; i++)
+      for (int i = 0; i < C::MT; i++) {
+        const v4i w = {f.a[i][0], f.a[i][1], f.a[i][2], f.a[i][3]};
+        ah[i] = w & m;
+        al[i] = (w << 4) & m;
+      }
 #pragma unroll
-      for (int j = 0; j < C::NT; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * KS, (int)sc.a[i],
-                                                                    2 * KS, (int)sc.b[j]);
+      for (int j = 0; j < C::NT; j++) {
+        const v4i w = {f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3]};
+        bh[j] = w & m;
+        bl[j] = (w << 4) & m;
+      }
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah[i], bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al[i], bl[j], acc[i][j], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * KS, (int)sc.a[i],
+                                                                      2 * KS, (int)sc.b[j]);
+    }
   };
   typedef std::integral_constant<int, 0> Slice0;
   typedef std::integral_constant<int, 1> Slice1;
@@ -263,7 +303,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   // wave's reads of stage s-1 were consumed by MFMAs issued before it (NS = DIST + 2).
   static_assert(C::NS >= C::DIST + 2, "ring too shallow for the prefetch distance");
   constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
-  constexpr int NM = C::MT * C::NT;  // MFMAs per slice
+  constexpr int NM = C::MT * C::NT * (INTC ? 2 : 1);  // MFMAs per slice
   constexpr int P1 = NM - 1 < NR ? NM - 1 : NR;  // slice-1 reads paired with slice-0 MFMAs
   const int nst = p.kstages;
 
@@ -296,50 +336,19 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
         u.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + kk + 16 * h + 8 * g));
     }
   };
-  auto up_mma = [&](const UpOps& u) {
+  auto up_mma = [&](const UpOps& u, auto& F) {
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int i = 0; i < C::MT; i++)
 #pragma unroll
         for (int j = 0; j < C::NT; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u.a[h][i], u.b[h][j], acc[i][j], 0, 0, 0);
+          F[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u.a[h][i], u.b[h][j], F[i][j], 0, 0, 0);
   };
-  // A finished down (no split-K partials) is requested with plain loads before the first stages
-  // go out, so their wait before the MFMAs leaves the stages in flight; partials are summed as
-  // they arrive, so they are requested after the stages. Every launch has at least two stages.
-  UpOps u0;
-  const bool up_direct = p.down_chunks <= 1;
-  if (DT::is_bf16 && p.rp > 0 && up_direct) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-      for (int i = 0; i < C::MT; i++)
-        u0.a[h][i] = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const T*>(p.down) + (int64_t)drow[i] * p.rp + 16 * h + 8 * g));
-#pragma unroll
-      for (int j = 0; j < C::NT; j++)
-        u0.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + 16 * h + 8 * g));
-    }
-  }
-  static_assert(C::DIST == 2, "two stages issued here");
-  issue(0);
-  issue(1);
-  if constexpr (DT::is_bf16) {
-    if (p.rp > 0) {
-      if (!up_direct) up_load(u0, 0);
-      up_mma(u0);
-      for (int kk = 32; kk < p.rp; kk += 32) {
-        UpOps u;
-        up_load(u, kk);
-        up_mma(u);
-      }
-    }
-  } else {
-    // f32 io: down (finished, or the ordered sum of its split-K partials) and L2^T are split
-    // into bf16 high and low parts, and down L2 = dh lh + dh ll + dl lh on bf16 MFMAs (the
-    // dropped dl ll and the split leave a relative error near 2^-16). Requested after the first
-    // stages, so its waits cover them too.
+  // f32 io: down (finished, or the ordered sum of its split-K partials) and L2^T are split
+  // into bf16 high and low parts, and down L2 = dh lh + dh ll + dl lh on bf16 MFMAs (the
+  // dropped dl ll and the split leave a relative error near 2^-16).
+  auto up_f32 = [&](auto& F) {
     for (int kk = 0; kk < p.rp; kk += 16) {
       v8bf ah[C::MT], al[C::MT];
 #pragma unroll
@@ -358,15 +367,50 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
         split_bf16x8(v, bh, bl);
 #pragma unroll
         for (int i = 0; i < C::MT; i++) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh, acc[i][j], 0, 0, 0);
+          F[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh, F[i][j], 0, 0, 0);
+          F[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl, F[i][j], 0, 0, 0);
+          F[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh, F[i][j], 0, 0, 0);
         }
       }
     }
+  };
+  // A finished down (no split-K partials) is requested with plain loads before the first stages
+  // go out, so their wait before the MFMAs leaves the stages in flight; partials are summed as
+  // they arrive, so they are requested after the stages. Every launch has at least two stages.
+  UpOps u0;
+  const bool up_direct = p.down_chunks <= 1;
+  if (!INTC && DT::is_bf16 && p.rp > 0 && up_direct) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+        u0.a[h][i] = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const T*>(p.down) + (int64_t)drow[i] * p.rp + 16 * h + 8 * g));
+#pragma unroll
+      for (int j = 0; j < C::NT; j++)
+        u0.b[h][j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol[j] * p.rp + 16 * h + 8 * g));
+    }
+  }
+  static_assert(C::DIST == 2, "two stages issued here");
+  issue(0);
+  issue(1);
+  if constexpr (!INTC) {
+    if constexpr (DT::is_bf16) {
+      if (p.rp > 0) {
+        if (!up_direct) up_load(u0, 0);
+        up_mma(u0, acc);
+        for (int kk = 32; kk < p.rp; kk += 32) {
+          UpOps u;
+          up_load(u, kk);
+          up_mma(u, acc);
+        }
+      }
+    } else {
+      up_f32(acc);  // requested after the first stages, so its waits cover them too
+    }
   }
 
-  wait_stage<C::LOADS_PER_STAGE, C::DIST + 2>(nst - 1 < C::DIST - 1 ? nst - 1 : C::DIST - 1);
+  wait_stage<LPS, C::DIST + 2>(nst - 1 < C::DIST - 1 ? nst - 1 : C::DIST - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   Frag fa, fb, f1;
@@ -392,7 +436,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
     if constexpr (NM - 1 > P1) __builtin_amdgcn_sched_group_barrier(0x008, NM - 1 - P1, 0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (AHEAD >= 0) {
-      wait_vmcnt<C::LOADS_PER_STAGE * AHEAD>();
+      wait_vmcnt<LPS * AHEAD>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const uint8_t* nb = smem + ((s + 1) % C::NS) * C::STAGE;
@@ -427,83 +471,119 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   stage(nst - 2, fa, sa, fb, sb, LastButOne());
   stage(nst - 1, fb, sb, fa, sa, Last());
 
-  // ---- two-level scaling: alpha * (residual + down L2 / alpha), before the bias
-  if (p.alpha) {
-    const float al = p.alpha[0];
+  // ---- epilogue on fp32 accumulators F (named acc inside)
+  auto finish = [&](auto& acc) {
+    // ---- two-level scaling: alpha * (residual + down L2 / alpha), before the bias
+    if (p.alpha) {
+      const float al = p.alpha[0];
+  #pragma unroll
+      for (int i = 0; i < C::MT; i++)
+  #pragma unroll
+        for (int j = 0; j < C::NT; j++)
+  #pragma unroll
+          for (int v = 0; v < 16; v++) acc[i][j][v] *= al;
+    }
+
+    // ---- output bias (one column per lane and 32x32 tile)
+    if (p.bias) {
+  #pragma unroll
+      for (int j = 0; j < C::NT; j++) {
+        const float bz = bias_at<DT>(p.bias, n0 + wn * C::TN + 32 * j + l32, p.N);
+  #pragma unroll
+        for (int i = 0; i < C::MT; i++)
+  #pragma unroll
+          for (int v = 0; v < 16; v++) acc[i][j][v] += bz;
+      }
+    }
+
+    // ---- epilogue: one rounding, staged through the (now idle) LDS ring for 16-byte stores. In a
+    // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Each lane rounds
+    // rows (r, r+1) of its column into one word (e = 0, 2), neighbouring lanes swap those words
+    // (DPP quad_perm [1,0,3,2]), and one byte permute leaves the even lane row r of columns
+    // (l32, l32+1) and the odd lane row r+1 of the same two columns: one 4-byte LDS write per
+    // pair and no per-pair select.
+    if constexpr (!DT::is_bf16) {
+      store_f32_tile<BM, BN>(p, acc, smem, t, wm, wn, l32, g, m0, n0);
+      return;
+    }
+    static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
+    const bool odd = l32 & 1;
+    // perm(neighbour, own): bytes 0-3 are the own word, 4-7 the neighbour's; the even lane takes
+    // (own.lo, neighbour.lo), the odd lane (neighbour.hi, own.hi)
+    const u32 psel = odd ? 0x03020706u : 0x05040100u;
+    __syncthreads();
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* wtile = tile + (odd ? BN : 0);
+  #pragma unroll
+    for (int i = 0; i < C::MT; i++)
+  #pragma unroll
+      for (int j = 0; j < C::NT; j++) {
+        const int c = wn * C::TN + 32 * j + (l32 & ~1);
+  #pragma unroll
+        for (int q = 0; q < 4; q++)
+  #pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const u32 own = pack_bf16x2(acc[i][j][4 * q + e], acc[i][j][4 * q + e + 1]);
+            const u32 nb = (u32)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
+            const int r = wm * C::TM + 32 * i + 8 * q + 4 * g + e;
+            *reinterpret_cast<u32*>(wtile + r * BN + c) = __builtin_amdgcn_perm(nb, own, psel);
+          }
+      }
+    __syncthreads();
+    T* y = reinterpret_cast<T*>(p.y);
+    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+    const bool vec_ok = (p.ldy % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
+    for (int c = t; c < BM * CPR; c += 64 * C::NWV) {
+      const int r = c / CPR, cc = c - r * CPR;
+      const int row = m0 + r, col = n0 + cc * 8;
+      if (row >= p.B || col >= p.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + r * BN + cc * 8);
+      T* dst = y + (int64_t)row * p.ldy + col;
+      if (vec_ok && col + 8 <= p.N) {
+        // streaming store: the output is not read again here, so it should not push the operand
+        // stages that other tiles of this XCD still read out of L2
+        __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(dst));
+      } else {
+        const u32 w[4] = {v.x, v.y, v.z, v.w};
+  #pragma unroll
+        for (int q = 0; q < 8; q++)
+          if (col + q < p.N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+      }
+    }
+  };
+  if constexpr (INTC) {
+    // exact int32 sums (256 times the code products) to fp32, then the up-projection
+    v16f facc[C::MT][C::NT];
+    const float scl = p.sx[0] * p.sr[0];
 #pragma unroll
     for (int i = 0; i < C::MT; i++)
 #pragma unroll
       for (int j = 0; j < C::NT; j++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) acc[i][j][v] *= al;
-  }
-
-  // ---- output bias (one column per lane and 32x32 tile)
-  if (p.bias) {
-#pragma unroll
-    for (int j = 0; j < C::NT; j++) {
-      const float bz = bias_at<DT>(p.bias, n0 + wn * C::TN + 32 * j + l32, p.N);
-#pragma unroll
-      for (int i = 0; i < C::MT; i++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) acc[i][j][v] += bz;
-    }
-  }
-
-  // ---- epilogue: one rounding, staged through the (now idle) LDS ring for 16-byte stores. In a
-  // 32x32 tile lane (l32, g) holds column l32 of rows 8q + 4g + e (e = 0..3). Each lane rounds
-  // rows (r, r+1) of its column into one word (e = 0, 2), neighbouring lanes swap those words
-  // (DPP quad_perm [1,0,3,2]), and one byte permute leaves the even lane row r of columns
-  // (l32, l32+1) and the odd lane row r+1 of the same two columns: one 4-byte LDS write per
-  // pair and no per-pair select.
-  if constexpr (!DT::is_bf16) {
-    store_f32_tile<BM, BN>(p, acc, smem, t, wm, wn, l32, g, m0, n0);
-    return;
-  }
-  static_assert(BM * BN * 2 <= C::SMEM, "output tile must fit the LDS ring");
-  const bool odd = l32 & 1;
-  // perm(neighbour, own): bytes 0-3 are the own word, 4-7 the neighbour's; the even lane takes
-  // (own.lo, neighbour.lo), the odd lane (neighbour.hi, own.hi)
-  const u32 psel = odd ? 0x03020706u : 0x05040100u;
-  __syncthreads();
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* wtile = tile + (odd ? BN : 0);
-#pragma unroll
-  for (int i = 0; i < C::MT; i++)
-#pragma unroll
-    for (int j = 0; j < C::NT; j++) {
-      const int c = wn * C::TN + 32 * j + (l32 & ~1);
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const u32 own = pack_bf16x2(acc[i][j][4 * q + e], acc[i][j][4 * q + e + 1]);
-          const u32 nb = (u32)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
-          const int r = wm * C::TM + 32 * i + 8 * q + 4 * g + e;
-          *reinterpret_cast<u32*>(wtile + r * BN + c) = __builtin_amdgcn_perm(nb, own, psel);
-        }
-    }
-  __syncthreads();
-  T* y = reinterpret_cast<T*>(p.y);
-  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-  const bool vec_ok = (p.ldy % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
-  for (int c = t; c < BM * CPR; c += 64 * C::NWV) {
-    const int r = c / CPR, cc = c - r * CPR;
-    const int row = m0 + r, col = n0 + cc * 8;
-    if (row >= p.B || col >= p.N) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * BN + cc * 8);
-    T* dst = y + (int64_t)row * p.ldy + col;
-    if (vec_ok && col + 8 <= p.N) {
-      // streaming store: the output is not read again here, so it should not push the operand
-      // stages that other tiles of this XCD still read out of L2
-      __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(dst));
+        for (int v = 0; v < 16; v++) facc[i][j][v] = ((float)acc[i][j][v] * 0x1p-8f) * scl;
+    if constexpr (DT::is_bf16) {
+      for (int kk = 0; kk < p.rp; kk += 32) {
+        UpOps u;
+        up_load(u, kk);
+        up_mma(u, facc);
+      }
     } else {
-      const u32 w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 8; q++)
-        if (col + q < p.N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+      up_f32(facc);
     }
+    finish(facc);
+  } else {
+    finish(acc);
   }
+}
+
+template <class DT, int BM, int BN>
+__global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
+  gemm_big<DT, BM, BN, false>(p);
+}
+
+template <class DT, int BM, int BN>
+__global__ __launch_bounds__(512) void k_gemm_int_big(GemmParams p) {
+  gemm_big<DT, BM, BN, true>(p);
 }
 
 }  // namespace dev
@@ -524,6 +604,25 @@ static hipError_t launch_mx_dt(const GemmParams& p, hipStream_t stream) {
   return launch_gemm_kernel(k_gemm_mx<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
+template <class DT, int BM, int BN>
+static hipError_t launch_int_big_dt(const GemmParams& p, hipStream_t stream) {
+  typedef MxCfg<BM, BN> C;
+  const int tiles = ((p.B + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int_big<DT, BM, BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  return launch_gemm_kernel(k_gemm_int_big<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
+}
+
+template <int BM, int BN>
+static hipError_t launch_int_big_t(const GemmParams& p, int dtype, hipStream_t stream) {
+  return dtype == SVDQ_BF16 ? launch_int_big_dt<BF16, BM, BN>(p, stream) : launch_int_big_dt<F32, BM, BN>(p, stream);
+}
+
 // Compute units of the current device (looked up once per device; 256 if the query fails).
 static int64_t device_cus() {
   static std::atomic<int> cus[64];
@@ -541,6 +640,24 @@ static int64_t device_cus() {
     cus[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+// Index into {128x192, 128x256, 256x192, 256x256} of the tile with the least estimated time:
+// rounds of the chip x (10 us + us_per_elem per output element of the tile); 192-wide tiles
+// only when N % 192 == 0; the first of equal estimates wins.
+static int pick_tile(const GemmParams& p, int64_t cus, double us_per_elem) {
+  const int cand[4][2] = {{128, 192}, {128, 256}, {256, 192}, {256, 256}};
+  int best = -1;
+  double best_t = 0;
+  for (int c = 0; c < 4; c++) {
+    const int bm = cand[c][0], bn = cand[c][1];
+    if (bn == 192 && p.N % 192 != 0) continue;
+    const int64_t tiles = ((int64_t)(p.B + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const double t = (double)rounds * (10.0 + us_per_elem * bm * bn);
+    if (best < 0 || t < best_t) best = c, best_t = t;
+  }
+  return best;
 }
 
 template <int BM, int BN>
@@ -564,22 +681,35 @@ hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stre
   // busy); 192-wide tiles only when N is a multiple of 192. At 4096 rows this picks 256x256 for
   // N = 12288 and 256x192 for N = 3072; at 512 rows or fewer, 128-row tiles.
   const int64_t cus = device_cus();
-  int best = -1;
-  double best_t = 0;
-  const int cand[4][2] = {{128, 192}, {128, 256}, {256, 192}, {256, 256}};
-  for (int c = 0; c < 4; c++) {
-    const int bm = cand[c][0], bn = cand[c][1];
-    if (bn == 192 && p.N % 192 != 0) continue;
-    const int64_t tiles = ((int64_t)(p.B + bm - 1) / bm) * ((p.N + bn - 1) / bn);
-    const int64_t rounds = (tiles + cus - 1) / cus;
-    const double t = (double)rounds * (10.0 + 0.3e-3 * bm * bn);
-    if (best < 0 || t < best_t) best = c, best_t = t;
-  }
-  switch (best) {
+  switch (pick_tile(p, cus, 0.3e-3)) {
     case 0: return launch_mx_t<128, 192>(p, dtype, stream);
     case 1: return launch_mx_t<128, 256>(p, dtype, stream);
     case 2: return launch_mx_t<256, 192>(p, dtype, stream);
     default: return launch_mx_t<256, 256>(p, dtype, stream);
+  }
+}
+
+// Per-tensor INT with nibble codes (at most 4 bits) on the large tiles; hipErrorNotSupported
+// when the 64 x 64 INT kernel serves the shape better, or an operand array is past 2 GiB.
+// Measured at M = N = 4096 (whole calls): the 64 x 64 kernel takes ~10 us per round of the
+// chip and wins up to two rounds (512 rows: 35 us against 39 for the best large tile); from
+// four rounds on the large tiles win (1024 rows: 49 us against 55, 4096 rows: 90 against 168).
+// Among the large tiles the same estimate as for MXFP4 picks the shape, with twice the MFMA
+// time per output element (the int8 rate is half the FP4 rate).
+hipError_t launch_gemm_int_big(const GemmParams& p0, int bits, int dtype, hipStream_t stream) {
+  if (bits > 4) return hipErrorNotSupported;
+  const int64_t cus = device_cus();
+  if (((int64_t)(p0.B + 63) / 64) * ((p0.N + 63) / 64) < 4 * cus) return hipErrorNotSupported;
+  GemmParams p = p0;
+  p.kstages = p.kq;  // 128-code stages of 64 bytes per row
+  if (p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.ldw >= lim) return hipErrorNotSupported;
+  switch (pick_tile(p, cus, 0.6e-3)) {
+    case 0: return launch_int_big_t<128, 192>(p, dtype, stream);
+    case 1: return launch_int_big_t<128, 256>(p, dtype, stream);
+    case 2: return launch_int_big_t<256, 192>(p, dtype, stream);
+    default: return launch_int_big_t<256, 256>(p, dtype, stream);
   }
 }
 

@@ -119,3 +119,9 @@ def test_measured_ceiling(tmp_path):
         assert m["probe"] == probe and m["peak"] == peak
         assert m["frac"] == pytest.approx(r["achieved"] / peak)
     assert bench.measured_ceiling(WORKLOADS[4], r, str(tmp_path / "absent.json")) is None
+
+
+@pytest.mark.parametrize("B,kernel", [(256, "k_gemm_int4"), (512, "k_gemm_int4"), (1024, "k_gemm_int_big"), (4096, "k_gemm_int_big")])
+def test_int_routing_by_batch(B, kernel):
+    """INT4 at 4096 x 4096: 64 x 64 tiles up to three rounds of the chip, the large tiles from four."""
+    assert bench.gemm_kernel(WORKLOADS[2], B)[0] == kernel

@@ -277,18 +277,23 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
     rules of the library, restated so that each exact case below names the kernel it aims at."""
     if fmt == "mx" and B <= 64:
         return "decode"
-    if fmt == "mx":
-        # fewest rounds of 256 compute units x per-round time 10 us + 0.3 ns per tile element;
-        # 192-wide tiles only when N % 192 == 0; the first of equal estimates wins
+    def pick(prefix, us_per_elem):
+        # fewest rounds of 256 compute units x per-round time 10 us + us_per_elem per tile
+        # element; 192-wide tiles only when N % 192 == 0; the first of equal estimates wins
         best = None
         for bm, bn in ((128, 192), (128, 256), (256, 192), (256, 256)):
             if bn == 192 and N % 192:
                 continue
             rounds = -(-(-(-B // bm) * -(-N // bn)) // 256)
-            t = rounds * (10.0 + 0.3e-3 * bm * bn)
+            t = rounds * (10.0 + us_per_elem * bm * bn)
             if best is None or t < best[0]:
-                best = (t, f"mx{bm}x{bn}")
+                best = (t, f"{prefix}{bm}x{bn}")
         return best[1]
+    if fmt == "mx":
+        return pick("mx", 0.3e-3)
+    # INT nibble codes take the large tiles once the 64 x 64 kernel needs four rounds
+    if bits <= 4 and -(-B // 64) * -(-N // 64) >= 4 * 256:
+        return pick("int", 0.6e-3)
     return "int4" if bits <= 4 else "int8"
 
 
@@ -335,6 +340,49 @@ def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
     got = _np(y)
     bad = np.argwhere(_bits(got) != _bits(want))
     assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("B,M,N,route,dtype", [
+    (1024, 256, 4096, "int128x256", "bf16"),   # four rounds of 64 x 64 tiles: the large tiles take over
+    (1100, 320, 4000, "int128x256", "bf16"),   # ragged B and N, four K stages
+    (2048, 256, 3072, "int128x192", "bf16"),
+    (4096, 256, 3072, "int256x192", "f32"),    # float32 io (its f32 tile leaves in row chunks)
+    (4096, 256, 4096, "int256x256", "bf16"),
+])
+def test_int_large_tile_exact_special_case(B, M, N, route, dtype):
+    """INT4 exact case (rank 0, unit scale, integer x and W with max |.| = 7) through each tile
+    of the large-tile INT kernel: nibbles unpacked to int8 times 16 on the int8 MFMAs, exact
+    int32 sums, Y = x @ W bit for bit."""
+    assert _gemm_route(B, M, N, "int", 4, dtype) == route
+    rng = np.random.default_rng(B + N)
+    x = rng.integers(-7, 8, (B, M)).astype(np.float32)
+    w = rng.integers(-7, 8, (M, N)).astype(np.float32)
+    x[0, 0] = w[0, 0] = 7
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, 4, "int")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x.astype(np.float64) @ w.astype(np.float64), dtype)
+    bad = np.argwhere(_bits(_np(y)) != _bits(want))
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("B,M,N,rank,dtype", [
+    (1024, 2048, 4096, 32, "bf16"),
+    (4096, 1024, 4096, 64, "bf16"),
+    (2048, 768, 3072, 96, "f32"),
+])
+def test_int_large_tile_shapes(B, M, N, rank, dtype):
+    """The large-tile INT kernel with a low-rank branch (up-projection after the K loop, on the
+    dequantised accumulators) against the oracle."""
+    assert _gemm_route(B, M, N, "int", 4, dtype) not in ("int4", "int8")
+    rng = np.random.default_rng(B + M + rank)
+    x = O.to_dtype(rng.standard_normal((B, M)), dtype)
+    w = O.to_dtype(0.02 * rng.standard_normal((M, N)) + 0.05 * rng.standard_normal((M, 3)) @ rng.standard_normal((3, N)), dtype)
+    from workloads import smoothing_scale
+    s = smoothing_scale(x, w, 0.5)
+    p = R.prepare(_g(w, dtype), torch.from_numpy(s), rank, 4, "int", keep_factors=True)
+    y = R.linear(_g(x, dtype), p)
+    ref = O.forward_ref(x, s, _np(p.left), _np(p.right), _np(p.residual), "int", 4, dtype)
+    assert O.rel_fro(_np(y), ref) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("B,M,N,route", [
