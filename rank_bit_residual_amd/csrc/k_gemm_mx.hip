@@ -1,4 +1,5 @@
-// Residual GEMM for MXFP4 at large batch on gfx950 (step (c) of the operator):
+// Residual GEMM at large batch on gfx950 (step (c) of the operator), for MXFP4 (k_gemm_mx)
+// and for per-tensor INT4 (k_gemm_int_big, the same body on int8 MFMAs; see gemm_big):
 //   Y = D( Q(X^) Q(R) + down L2 )
 // Q(X^) and Q(R) are E2M1 codes with one E8M0 scale per 32 elements along K; the product runs
 // on v_mfma_scale_f32_32x32x64_f8f6f4 (each lane's 32 K-contiguous FP4 values scaled by its own
