@@ -42,8 +42,8 @@ def gemm_kernel(wl, B):
     if wl.fmt == "mx" and wl.dtype == "bf16" and B > 64:
         return "k_gemm_mx", os.path.join(CSRC, "k_gemm_mx.hip")
     if wl.fmt == "int":
-        # nibble codes take the large tiles once 64 x 64 tiles would need four rounds of 256 CUs
-        if wl.bits <= 4 and -(-B // 64) * -(-wl.N // 64) >= 4 * 256:
+        # the large tiles once 64 x 64 tiles would need four rounds of 256 CUs
+        if -(-B // 64) * -(-wl.N // 64) >= 4 * 256:
             return "k_gemm_int_big", os.path.join(CSRC, "k_gemm_mx.hip")
         return "k_gemm_int4", os.path.join(CSRC, "k_gemm_int.hip")
     # the MXFP4 kernels cover every shape of these workloads (arrays under 2 GiB)

@@ -115,12 +115,14 @@ __device__ __forceinline__ void store_f32_tile(const GemmParams& p, const v16f (
 }
 
 // One BM x BN tile of the residual GEMM. INTC = false: MXFP4 (FP4 codes with E8M0 scales,
-// weight codes tiled 16 columns x 128 codes per 1 KB). INTC = true: per-tensor INT with nibble
-// codes (both operands row-major, K-contiguous; no per-block scales): each FP4 MFMA's slot
-// becomes two int8 MFMAs on the odd and even codes (a nibble in the high half of a byte reads
-// as 16 times the code), accumulated exactly in int32 and dequantised by s_x s_R / 256 after
-// the K loop, where the up-projection follows.
-template <class DT, int BM, int BN, bool INTC>
+// weight codes tiled 16 columns x 128 codes per 1 KB). INTC = true: per-tensor INT, both
+// operands row-major and K-contiguous, no per-block scales, a stage still 64 bytes per row.
+// NIB (nibble codes, 128 per stage): each FP4 MFMA's slot becomes two int8 MFMAs on the odd
+// and even codes (a nibble in the high half of a byte reads as 16 times the code); int8 codes
+// (64 per stage): one int8 MFMA on the 16 codes of the lane's chunk. Sums are exact in int32
+// and dequantised (by s_x s_R, and 2^-8 for nibbles) after the K loop, where the
+// up-projection follows.
+template <class DT, int BM, int BN, bool INTC, bool NIB = true>
 __device__ __forceinline__ void gemm_big(const GemmParams& p) {
   typedef MxCfg<BM, BN> C;
   typedef typename DT::T T;
@@ -196,7 +198,8 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
     for (int j = 0; j < C::A_PER_WAVE; j++) buffer_to_lds16(p.acodes, (int)((int64_t)p.B * p.lda), base + a_dst[j], a_off[j], st * C::SB);
 #pragma unroll
     for (int j = 0; j < C::B_PER_WAVE; j++)
-      buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * p.kq * 64), base + b_dst[j], b_off[j], st * (INTC ? C::SB : 1024));
+      buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * (INTC ? p.ldw : (int64_t)p.kq * 64)), base + b_dst[j], b_off[j],
+                      st * (INTC ? C::SB : 1024));
     if constexpr (!INTC) {
       if (wave < 4)
         buffer_to_lds4(p.ascales, (int)((int64_t)p.ascale_groups * p.kq * 256), base + s_off_a + sw * 256, sa_off, st * 256);
@@ -258,7 +261,15 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
   };
   auto mma = [&](const Frag& f, const Scales& sc, auto ks_c) {
     constexpr int KS = decltype(ks_c)::value;
-    if constexpr (INTC) {
+    if constexpr (INTC && !NIB) {
+      // lane (l32, g) holds the 16 int8 codes of chunk 2 KS + g: one 32x32x32 MFMA
+#pragma unroll
+      for (int i = 0; i < C::MT; i++)
+#pragma unroll
+        for (int j = 0; j < C::NT; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{f.a[i][0], f.a[i][1], f.a[i][2], f.a[i][3]},
+                                                           v4i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3]}, acc[i][j], 0, 0, 0);
+    } else if constexpr (INTC) {
       // lane (l32, g) holds 32 nibble codes of K block 2 KS + g: odd codes (w & 0xF0F0F0F0)
       // and even codes ((w << 4) & 0xF0F0F0F0) as int8 times 16, one 32x32x32 MFMA each
       const v4i m = {(int)0xF0F0F0F0, (int)0xF0F0F0F0, (int)0xF0F0F0F0, (int)0xF0F0F0F0};
@@ -304,7 +315,7 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
   // wave's reads of stage s-1 were consumed by MFMAs issued before it (NS = DIST + 2).
   static_assert(C::NS >= C::DIST + 2, "ring too shallow for the prefetch distance");
   constexpr int NR = C::MT + C::NT;  // 16-byte operand reads per slice
-  constexpr int NM = C::MT * C::NT * (INTC ? 2 : 1);  // MFMAs per slice
+  constexpr int NM = C::MT * C::NT * (INTC && NIB ? 2 : 1);  // MFMAs per slice
   constexpr int P1 = NM - 1 < NR ? NM - 1 : NR;  // slice-1 reads paired with slice-0 MFMAs
   const int nst = p.kstages;
 
@@ -561,7 +572,7 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
 #pragma unroll
       for (int j = 0; j < C::NT; j++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) facc[i][j][v] = ((float)acc[i][j][v] * 0x1p-8f) * scl;
+        for (int v = 0; v < 16; v++) facc[i][j][v] = ((float)acc[i][j][v] * (NIB ? 0x1p-8f : 1.0f)) * scl;
     if constexpr (DT::is_bf16) {
       for (int kk = 0; kk < p.rp; kk += 32) {
         UpOps u;
@@ -582,9 +593,9 @@ __global__ __launch_bounds__(512) void k_gemm_mx(GemmParams p) {
   gemm_big<DT, BM, BN, false>(p);
 }
 
-template <class DT, int BM, int BN>
+template <class DT, int BM, int BN, bool NIB>
 __global__ __launch_bounds__(512) void k_gemm_int_big(GemmParams p) {
-  gemm_big<DT, BM, BN, true>(p);
+  gemm_big<DT, BM, BN, true, NIB>(p);
 }
 
 }  // namespace dev
@@ -605,23 +616,24 @@ static hipError_t launch_mx_dt(const GemmParams& p, hipStream_t stream) {
   return launch_gemm_kernel(k_gemm_mx<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
-template <class DT, int BM, int BN>
+template <class DT, int BM, int BN, bool NIB>
 static hipError_t launch_int_big_dt(const GemmParams& p, hipStream_t stream) {
   typedef MxCfg<BM, BN> C;
   const int tiles = ((p.B + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int_big<DT, BM, BN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_int_big<DT, BM, BN, NIB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  return launch_gemm_kernel(k_gemm_int_big<DT, BM, BN>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
+  return launch_gemm_kernel(k_gemm_int_big<DT, BM, BN, NIB>, dim3(tiles), dim3(64 * C::NWV), C::SMEM, stream, p);
 }
 
 template <int BM, int BN>
-static hipError_t launch_int_big_t(const GemmParams& p, int dtype, hipStream_t stream) {
-  return dtype == SVDQ_BF16 ? launch_int_big_dt<BF16, BM, BN>(p, stream) : launch_int_big_dt<F32, BM, BN>(p, stream);
+static hipError_t launch_int_big_t(const GemmParams& p, bool nib, int dtype, hipStream_t stream) {
+  if (nib) return dtype == SVDQ_BF16 ? launch_int_big_dt<BF16, BM, BN, true>(p, stream) : launch_int_big_dt<F32, BM, BN, true>(p, stream);
+  return dtype == SVDQ_BF16 ? launch_int_big_dt<BF16, BM, BN, false>(p, stream) : launch_int_big_dt<F32, BM, BN, false>(p, stream);
 }
 
 // Compute units of the current device (looked up once per device; 256 if the query fails).
@@ -690,27 +702,29 @@ hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stre
   }
 }
 
-// Per-tensor INT with nibble codes (at most 4 bits) on the large tiles; hipErrorNotSupported
-// when the 64 x 64 INT kernel serves the shape better, or an operand array is past 2 GiB.
-// Measured at M = N = 4096 (whole calls): the 64 x 64 kernel takes ~10 us per round of the
-// chip and wins up to two rounds (512 rows: 35 us against 39 for the best large tile); from
-// four rounds on the large tiles win (1024 rows: 49 us against 55, 4096 rows: 90 against 168).
-// Among the large tiles the same estimate as for MXFP4 picks the shape, with twice the MFMA
-// time per output element (the int8 rate is half the FP4 rate).
+// Per-tensor INT on the large tiles (nibble codes of at most 4 bits, 128 per stage, or int8
+// codes of 5-8 bits, 64 per stage); hipErrorNotSupported when the 64 x 64 INT kernel serves
+// the shape better, or an operand array is past 2 GiB. Measured at M = N = 4096 (whole calls,
+// 4-bit codes): the 64 x 64 kernel takes ~10 us per round of the chip and wins up to two
+// rounds (512 rows: 35 us against 39 for the best large tile); from four rounds on the large
+// tiles win (1024 rows: 49 us against 55, 4096 rows: 90 against 168). Among the large tiles
+// the same estimate as for MXFP4 picks the shape, with twice the MFMA time per output element
+// (the int8 rate is half the FP4 rate).
 hipError_t launch_gemm_int_big(const GemmParams& p0, int bits, int dtype, hipStream_t stream) {
-  if (bits > 4) return hipErrorNotSupported;
+  if (bits > 8) return hipErrorNotSupported;
+  const bool nib = bits <= 4;
   const int64_t cus = device_cus();
   if (((int64_t)(p0.B + 63) / 64) * ((p0.N + 63) / 64) < 4 * cus) return hipErrorNotSupported;
   GemmParams p = p0;
-  p.kstages = p.kq;  // 128-code stages of 64 bytes per row
-  if (p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
+  p.kstages = (int)(p.ldw / 64);  // stages of 64 bytes per row: 128 nibble or 64 int8 codes
+  if (p.ldw % 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
   const int64_t lim = (int64_t)1 << 31;
   if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.ldw >= lim) return hipErrorNotSupported;
   switch (pick_tile(p, cus, 0.6e-3)) {
-    case 0: return launch_int_big_t<128, 192>(p, dtype, stream);
-    case 1: return launch_int_big_t<128, 256>(p, dtype, stream);
-    case 2: return launch_int_big_t<256, 192>(p, dtype, stream);
-    default: return launch_int_big_t<256, 256>(p, dtype, stream);
+    case 0: return launch_int_big_t<128, 192>(p, nib, dtype, stream);
+    case 1: return launch_int_big_t<128, 256>(p, nib, dtype, stream);
+    case 2: return launch_int_big_t<256, 192>(p, nib, dtype, stream);
+    default: return launch_int_big_t<256, 256>(p, nib, dtype, stream);
   }
 }
 

@@ -102,7 +102,7 @@ hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stre
 // Per-tensor INT: 64x64 tiles, K split over the waves of a block (kstages = Kp/256 for nibble
 // codes, Kp/128 for int8 codes; any K).
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream);
-// Per-tensor INT with nibble codes on the large-batch tiles; hipErrorNotSupported (nothing
+// Per-tensor INT (nibble or int8 codes) on the large-batch tiles; hipErrorNotSupported (nothing
 // launched) when the shape is better served by launch_gemm_int4.
 hipError_t launch_gemm_int_big(const GemmParams& p, int bits, int dtype, hipStream_t stream);
 // MXFP4, B <= 64 (bf16 or f32 io): K split over waves, weights streamed straight into registers.

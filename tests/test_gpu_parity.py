@@ -291,8 +291,8 @@ def _gemm_route(B, M, N, fmt, bits, dtype):
         return best[1]
     if fmt == "mx":
         return pick("mx", 0.3e-3)
-    # INT nibble codes take the large tiles once the 64 x 64 kernel needs four rounds
-    if bits <= 4 and -(-B // 64) * -(-N // 64) >= 4 * 256:
+    # INT takes the large tiles once the 64 x 64 kernel needs four rounds
+    if -(-B // 64) * -(-N // 64) >= 4 * 256:
         return pick("int", 0.6e-3)
     return "int4" if bits <= 4 else "int8"
 
@@ -339,6 +339,28 @@ def test_int4_kernel_exact_special_case(B, M, N, bits, dtype):
     want = O.to_dtype(x.astype(np.float64) @ w.astype(np.float64), dtype)
     got = _np(y)
     bad = np.argwhere(_bits(got) != _bits(want))
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("B,M,N,bits,route,dtype", [
+    (1024, 768, 4096, 8, "int128x256", "bf16"),  # int8 codes: 64 per stage, one MFMA per chunk
+    (4096, 512, 3072, 6, "int256x192", "f32"),
+    (1100, 256, 4000, 5, "int128x256", "bf16"),  # ragged B and N, four stages of 64 codes
+])
+def test_int8_codes_large_tile_exact_special_case(B, M, N, bits, route, dtype):
+    """Rank 0, unit scale, integer x and W with max |.| = qmax through the large-tile INT kernel
+    with int8 codes (5-8 bits): Y = x @ W bit for bit (|Y| <= qmax^2 K < 2^24)."""
+    q = 2 ** (bits - 1) - 1
+    assert q * q * M < 2 ** 24
+    assert _gemm_route(B, M, N, "int", bits, dtype) == route
+    rng = np.random.default_rng(B + N + bits)
+    x = rng.integers(-q, q + 1, (B, M)).astype(np.float32)
+    w = rng.integers(-q, q + 1, (M, N)).astype(np.float32)
+    x[0, 0] = w[0, 0] = q
+    p = R.prepare(_g(w, dtype), torch.ones(M), 0, bits, "int")
+    y = R.linear(_g(x, dtype), p)
+    want = O.to_dtype(x.astype(np.float64) @ w.astype(np.float64), dtype)
+    bad = np.argwhere(_bits(_np(y)) != _bits(want))
     assert bad.size == 0, f"{len(bad)} outputs differ, first at {tuple(bad[0])}"
 
 
