@@ -974,7 +974,26 @@ def _sweep_cases(n=24, seed=2026):
     return out
 
 
-@pytest.mark.parametrize("c,B,M,N,rank,fmt,bits,dtype,bias", _sweep_cases())
+def _sweep_cases_large(n=8, seed=2027):
+    """Larger ragged shapes from a fixed seed, for the large-batch routes: B in [700, 4200], N in
+    [1000, 4200] (so INT takes the large tiles whenever 64 x 64 tiles would need four rounds,
+    and MXFP4 meets every tile shape), M in [64, 800], rank in [0, 64], INT widths 2-8, both
+    dtypes, a bias on every third case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        fmt = "mx" if c % 2 else "int"
+        dtype = "f32" if c % 3 == 1 else "bf16"
+        bits = 4 if fmt == "mx" else int(rng.integers(2, 9))
+        B = int(rng.integers(700, 4201))
+        M = int(rng.integers(64, 801))
+        N = int(rng.integers(1000, 4201))
+        rank = int(rng.integers(0, 65))
+        out.append((100 + c, B, M, N, rank, fmt, bits, dtype, c % 3 == 0))
+    return out
+
+
+@pytest.mark.parametrize("c,B,M,N,rank,fmt,bits,dtype,bias", _sweep_cases() + _sweep_cases_large())
 def test_parity_shape_sweep(c, B, M, N, rank, fmt, bits, dtype, bias):
     rng = np.random.default_rng(1000 + c)
     x = O.to_dtype(rng.standard_t(3, (B, M)), dtype)
