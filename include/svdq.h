@@ -232,8 +232,9 @@ int svdq_prepare_linear(const void* weight_nm, int64_t N, int64_t M, int64_t ldw
 /* --------------------------------------------------------------------------------------
  * Workspace of svdq_linear / svdq_quantize_activations: device scratch the caller
  * allocates once (any contents; nothing needs zeroing) and may reuse across calls that are
- * ordered on one stream. Holds activation codes [B, Kp/2] (int8 [B,Kp] for INT bits>4),
- * MX scales [B, Kp/32], the down-projection [B, rp], its split-K partials, the
+ * ordered on one stream. Holds activation codes [B, Kp/2] (int8 [B,Kp] for INT bits>4;
+ * for MX above 64 rows svdq_linear stores them in 1 KB tiles of 16 rows x 128 codes, rows
+ * rounded up to 16), MX scales [B, Kp/32], the down-projection [B, rp], its split-K partials, the
  * per-tensor INT maxima and (svdq_quantize_activations) the reciprocals of the scale.
  * Errors: EINVAL, EDTYPE.
  * ------------------------------------------------------------------------------------ */

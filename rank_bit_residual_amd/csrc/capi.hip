@@ -46,7 +46,7 @@ void workspace_layout(const Dims& d, const LaunchPlan& p, int64_t off[WS_NSEC]) 
     o = round_up(o + bytes, kAlign);
   };
   const int64_t B = p.B;
-  sec(WS_CODES, B * d.code_row_bytes());
+  sec(WS_CODES, round_up(B, 16) * d.code_row_bytes());  // tiled MX codes fill whole 16-row tiles
   sec(WS_SCALES, d.fmt == SVDQ_FMT_MX ? round_up(B, 64) * d.mx_scale_row_bytes() : 0);  // stage-tiled
   sec(WS_DOWN, B * d.rp * (int64_t)dtype_size(d.dtype));
   sec(WS_PARTIAL, p.k_chunks > 1 ? (int64_t)p.k_chunks * B * d.rp * 4 : 0);
@@ -348,11 +348,8 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   p.x_vec_ok = aligned(x, 16) && (ldx * (int64_t)dtype_size(dtype)) % 16 == 0;
   const float* glob = (const float*)(bl + boff[SVDQ_SEC_GLOBAL]);  // {g_x, g_R, alpha, 0}
   if (fmt == SVDQ_FMT_MX) p.gscale = glob;
-  tm.begin(1);
-  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, pl.rchunk, s), "activation quantise launch")))
-    return st;
-  tm.end(1);
-  // (c): residual GEMM + epilogue
+  // (c)'s parameters come first: the large-batch MXFP4 GEMM reads the activation codes in
+  // 16-row tiles, which the activation kernel then writes
   GemmParams g{};
   g.acodes = ws + woff[WS_CODES];
   g.lda = d.code_row_bytes();
@@ -377,11 +374,22 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
   g.N = (int)N;
   g.kstages = (int)(d.code_row_bytes() / 128);
   g.npad = (int)d.Np;
+  if (fmt == SVDQ_FMT_MX && B > 64) {
+    g.kstages = (int)(d.code_row_bytes() / 64);
+    g.acodes_tiled = mx_large_accepts(g) ? 1 : 0;
+    g.kstages = (int)(d.code_row_bytes() / 128);
+  }
+  p.codes_tiled = g.acodes_tiled;
+  tm.begin(1);
+  if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, pl.rchunk, s), "activation quantise launch")))
+    return st;
+  tm.end(1);
   tm.gemm_begin();
   hipError_t ge = hipErrorNotSupported;
   if (fmt == SVDQ_FMT_MX) {
     g.kstages = (int)(d.code_row_bytes() / 64);  // 64-byte stages
     ge = B <= 64 ? launch_gemm_mx_decode(g, dtype, s) : launch_gemm_mx_large(g, dtype, s);
+    if (ge == hipErrorNotSupported && g.acodes_tiled) return set_error(SVDQ_EHIP, "tiled activation codes left without their GEMM");
     if (ge == hipErrorNotSupported) g.kstages = (int)(d.code_row_bytes() / 128);
   }
   if (fmt == SVDQ_FMT_INT) {

@@ -579,7 +579,9 @@ __device__ __forceinline__ void act_finish(const ActParams& p, const ActLane& L,
           w4[q] = fp4_pack8(v, sc);
         }
       }
-      *reinterpret_cast<uint4*>(p.codes + (int64_t)L.b * p.ldc + k / 2) = uint4{w4[0], w4[1], w4[2], w4[3]};
+      const int64_t co = p.codes_tiled ? (((int64_t)(L.b >> 4) * (p.Kp >> 7) + (k >> 7)) << 10) + ((L.b & 15) << 6) + ((k & 127) >> 1)
+                                       : (int64_t)L.b * p.ldc + k / 2;
+      *reinterpret_cast<uint4*>(p.codes + co) = uint4{w4[0], w4[1], w4[2], w4[3]};
       const int64_t si = p.mxs_tiled ? mx_scale_tiled_index(L.b, k / 32, p.Kp / 128) : (int64_t)L.b * p.lds + k / 32;
       p.mxs[si] = (uint8_t)(e + 127);
     } else if constexpr (NIB) {

@@ -18,9 +18,10 @@
 // wave's loads of that stage visible and releases the buffer read in the previous iteration.
 // LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), so
 // the 16-byte reads of 16 consecutive rows (one LDS cycle of a ds_read_b128) hit distinct banks.
-// The prepared weight codes are tiled 16 columns x 128 codes per 1 KB, so each wave-wide load
-// of a B stage reads one contiguous kilobyte (the activation codes are row-major: 16 rows x 64
-// bytes per load).
+// The prepared weight codes are tiled 16 columns x 128 codes per 1 KB, and the activation
+// kernel writes the MXFP4 activation codes for this kernel in the same 1 KB tiles of 16 rows,
+// so each wave-wide load of a stage reads one contiguous kilobyte (INT operands are row-major:
+// 16 rows x 64 bytes per load).
 #include <atomic>
 #include <type_traits>
 
@@ -162,7 +163,8 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
     const int chunk = phys ^ ((row >> 2) & 3);
     int gr = m0 + row;
     gr = gr < p.B ? gr : p.B - 1;
-    a_off[j] = gr * p.lda + chunk * 16;
+    // MX: 16-row x 128-code tiles, + 1024 per stage; INT: row-major, + 64 per stage
+    a_off[j] = INTC ? gr * (int)p.lda + chunk * 16 : ((gr >> 4) * p.kq) * 1024 + (gr & 15) * 64 + chunk * 16;
     a_dst[j] = u * 1024;
   }
   int b_off[C::B_PER_WAVE], b_dst[C::B_PER_WAVE];
@@ -195,7 +197,8 @@ __device__ __forceinline__ void gemm_big(const GemmParams& p) {
   auto issue = [&](int st) {
     uint8_t* base = smem + (st % C::NS) * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::A_PER_WAVE; j++) buffer_to_lds16(p.acodes, (int)((int64_t)p.B * p.lda), base + a_dst[j], a_off[j], st * C::SB);
+    for (int j = 0; j < C::A_PER_WAVE; j++)
+      buffer_to_lds16(p.acodes, (int)((int64_t)((p.B + 15) & ~15) * p.lda), base + a_dst[j], a_off[j], st * (INTC ? C::SB : 1024));
 #pragma unroll
     for (int j = 0; j < C::B_PER_WAVE; j++)
       buffer_to_lds16(p.wcodes, (int)((int64_t)p.npad * (INTC ? p.ldw : (int64_t)p.kq * 64)), base + b_dst[j], b_off[j],
@@ -680,13 +683,17 @@ static hipError_t launch_mx_t(const GemmParams& p, int dtype, hipStream_t stream
 
 // MXFP4 path above decode batches (B > 64), bf16 or f32 io; returns hipErrorNotSupported when
 // an operand array is past 2 GiB, so the caller falls back to the general kernel.
-hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
-  if (p.B <= 64 || p.kstages < 2 || p.kstages % 2) return hipErrorNotSupported;
-  // the operand arrays are addressed through buffer resources with 32-bit offsets
+bool mx_large_accepts(const GemmParams& p) {
+  if (p.B <= 64 || p.kstages < 2 || p.kstages % 2) return false;
+  // the operand arrays (activation codes in whole 16-row tiles) are addressed through buffer
+  // resources with 32-bit offsets
   const int64_t lim = (int64_t)1 << 31;
-  if ((int64_t)p.B * p.lda >= lim || (int64_t)p.npad * p.kq * 64 >= lim ||
-      (int64_t)p.ascale_groups * p.kq * 256 >= lim || (int64_t)(p.npad >> 6) * p.kq * 256 >= lim)
-    return hipErrorNotSupported;
+  return !((int64_t)((p.B + 15) / 16) * 16 * p.lda >= lim || (int64_t)p.npad * p.kq * 64 >= lim ||
+           (int64_t)p.ascale_groups * p.kq * 256 >= lim || (int64_t)(p.npad >> 6) * p.kq * 256 >= lim);
+}
+
+hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream) {
+  if (!p.acodes_tiled || !mx_large_accepts(p)) return hipErrorNotSupported;
   // Tile shape: the candidate with the least estimated time, rounds of the chip x time per
   // round. A round (every compute unit on one tile) was measured at K = 3072 to take about
   // 10 us + 0.3 ns per output element of the tile: 128x192 17.4 us, 128x256 19.8, 256x192 24.7,

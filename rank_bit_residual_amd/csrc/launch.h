@@ -19,6 +19,10 @@ struct ActParams {
   uint8_t* mxs;  // MX scales: row-major [B][lds], or stage-tiled when mxs_tiled
   int64_t lds;
   int mxs_tiled;
+  // MX: codes in 1 KB tiles of 16 rows x 128 codes (tile (b / 16, k / 128) at
+  // ((b / 16) * Kp / 128 + k / 128) * 1024, row b % 16 at 64 (b % 16)) instead of row-major,
+  // for the large-batch MXFP4 GEMM; rows up to the next multiple of 16 must be allocated
+  int codes_tiled;
   const float* amax_part;  // INT: per-block maxima of |X^|
   int n_amax;
   int bits;
@@ -33,8 +37,9 @@ struct ActParams {
 };
 
 struct GemmParams {
-  const uint8_t* acodes;
+  const uint8_t* acodes;  // row-major [B][lda], or (MX, acodes_tiled) 16-row x 128-code tiles
   int64_t lda;
+  int acodes_tiled;
   const uint8_t* ascales;  // stage-tiled E8M0 bytes (see mx_scale_tiled_index)
   int ascale_groups;       // 64-row groups of the activation scales
   const uint8_t* wcodes;
@@ -97,8 +102,12 @@ hipError_t launch_gemm(const GemmParams& p, int fmt, int bits, int dtype, hipStr
 int calib_parts(int64_t B, int64_t M);
 hipError_t launch_calibrate(const void* x, int B, int M, int64_t ldx, const void* w, int N, int64_t ldw, int dtype,
                             double alpha, float* part, float* scale, hipStream_t stream);
-// Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered.
+// Large-batch MXFP4 kernel; hipErrorNotSupported (nothing launched) when the shape is not covered
+// (mx_large_accepts false) or the activation codes are not tiled.
 hipError_t launch_gemm_mx_large(const GemmParams& p, int dtype, hipStream_t stream);
+// Whether launch_gemm_mx_large takes this shape (p.kstages in 64-byte stages); the caller then
+// has the activation kernel write tiled codes.
+bool mx_large_accepts(const GemmParams& p);
 // Per-tensor INT: 64x64 tiles, K split over the waves of a block (kstages = Kp/256 for nibble
 // codes, Kp/128 for int8 codes; any K).
 hipError_t launch_gemm_int4(const GemmParams& p, int bits, int dtype, hipStream_t stream);
