@@ -255,6 +255,7 @@ __device__ inline void load_chan(const float* __restrict__ a, int k, int M, floa
 // Per-lane constants of a block.
 struct ActLane {
   int lane, i, g, b, rbase, nbl;
+  int xoff[4];  // full bf16 steps: element offsets (from the block's first row) of the lane's four x loads
   bool do_codes;
   float sx, ysx, qmax;
   float gx;  // MX two-level scaling: codes of RN(X^ g_x) (1 when not scaled)
@@ -317,18 +318,63 @@ struct FullIn {
   v4i bw[l1_ahead(RC) ? RC / 16 : 1][4];
 };
 
+// x of a full step, loaded by quads: in load q, the quad j of a 16-lane row g (lanes 4j..4j+3)
+// reads the 64 contiguous bytes of block g in row 4j + q, lane 4j + t taking the 16-byte piece
+// t. So each load covers 4 rows x 256 contiguous bytes (8 cache lines) instead of 16 rows x 4
+// scattered pieces (32 lines). Lane 4j + t then holds piece t of rows 4j..4j+3 and needs pieces
+// 0..3 of row 4j + t: a 4 x 4 transpose of (lane in quad, load) done by quad_transpose at use.
 template <int RC, bool LR, class T>
-__device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xrow, const ActLane& L, int k0,
+__device__ __forceinline__ void load_full(const ActParams& p, const T* __restrict__ xblk, const ActLane& L, int k0,
                                           FullIn<RC>& in) {
-  const uint4* src = reinterpret_cast<const uint4*>(xrow + k0 + 32 * L.g);
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    const uint4 w = src[q];
+    const uint4 w = *reinterpret_cast<const uint4*>(xblk + (L.xoff[q] + k0));
     in.raw[4 * q] = w.x; in.raw[4 * q + 1] = w.y; in.raw[4 * q + 2] = w.z; in.raw[4 * q + 3] = w.w;
   }
   in.y2 = *reinterpret_cast<const float2*>(p.recip + k0 + 2 * L.lane);
   in.s2 = *reinterpret_cast<const float2*>(p.scale + k0 + 2 * L.lane);
   if constexpr (l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, in.bw);
+}
+
+// The 4 x 4 transpose of load_full's pieces within each quad of lanes: afterwards lane t of a quad
+// holds in word 4 p + d what lane p held in word 4 t + d. Two butterfly rounds (lane and piece
+// bit 1, then bit 0), each swapping one word per piece pair with the partner lane (DPP
+// quad_perm, whole wave active).
+struct RawStep {
+  u32 raw[16];
+  float2 y2, s2;
+};
+// One butterfly round of quad_transpose: lanes and pieces whose bit M differ trade words.
+template <int M>
+__device__ __forceinline__ void quad_swap_round(u32 (&a)[16], int t) {
+  constexpr int CTRL = M == 2 ? 0x4E : 0xB1;  // quad_perm [2,3,0,1] or [1,0,3,2]
+  const bool hm = (t & M) != 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if (q & M) continue;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      // the partner's words of both pieces; a lane with bit M takes the partner's piece q | M
+      // in place of its piece q, a lane without it the partner's piece q in place of q | M
+      const u32 lo = a[4 * q + d], hi = a[4 * (q | M) + d];
+      const u32 p_hi = (u32)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, true);
+      const u32 p_lo = (u32)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, true);
+      a[4 * q + d] = hm ? p_hi : lo;
+      a[4 * (q | M) + d] = hm ? hi : p_lo;
+    }
+  }
+}
+template <int RC>
+__device__ __forceinline__ void quad_transpose(const FullIn<RC>& in, int lane, RawStep& out) {
+  u32 a[16];
+#pragma unroll
+  for (int w = 0; w < 16; w++) a[w] = in.raw[w];
+  quad_swap_round<2>(a, lane & 3);
+  quad_swap_round<1>(a, lane & 3);
+#pragma unroll
+  for (int w = 0; w < 16; w++) out.raw[w] = a[w];
+  out.y2 = in.y2;
+  out.s2 = in.s2;
 }
 
 // Full bf16 steps, exact path: X^ = RN_bf16(RN_f32(x / s)) for every element by div_markstein,
@@ -396,7 +442,7 @@ struct StepState {
 // First half of a step: loads, X^ = D(x / scale) and its block maximum.
 template <class DT, int FMT, bool NIB, bool FULL, int RC>
 __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT::T* __restrict__ xrow, const ActLane& L,
-                                           int k0, const FullIn<RC>& in, const v4i (&bwc)[RC / 16][4],
+                                           int k0, const FullIn<RC>& in_q, const v4i (&bwc)[RC / 16][4],
                                            StepState<DT, RC>& st) {
   typedef typename DT::T T;
   constexpr int RW = DT::is_bf16 ? 16 : 32;
@@ -430,7 +476,7 @@ __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT
 #pragma unroll
     for (int n = 0; n < NB; n++)
 #pragma unroll
-      for (int c = 0; c < 4; c++) bw[n][c] = in.bw[n][c];
+      for (int c = 0; c < 4; c++) bw[n][c] = in_q.bw[n][c];
   } else if constexpr (FAST) {
 #pragma unroll
     for (int n = 0; n < NB; n++)
@@ -444,6 +490,9 @@ __device__ __forceinline__ void act_smooth(const ActParams& p, const typename DT
   // final rounding to the dtype (rounding is monotone, so it rounds to max |X^|).
   float amax = 0.f;
   if constexpr (FAST) {
+    RawStep tin;
+    quad_transpose(in_q, L.lane, tin);
+    const RawStep& in = tin;
     u16x2 amax16 = {0, 0};
     if (__all(in.y2.x != 0.f && in.y2.y != 0.f)) {
       u16x2 band = {0xFFFF, 0xFFFF};
@@ -680,15 +729,24 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   static_assert(NW == 8, "the code split below pairs waves s and s + 4 of a SIMD");
   L.do_codes = p.codes != nullptr && (int)((wave / 4) % gridDim.z) == (int)blockIdx.z;
   const T* __restrict__ xrow = reinterpret_cast<const T*>(p.x) + (int64_t)bl * p.ldx;
+  // full bf16 steps load x by quads (load_full), from the block's first row; rows past B read
+  // row B - 1 like the lane's own row does
+  const T* __restrict__ xblk = reinterpret_cast<const T*>(p.x) + (int64_t)row0 * p.ldx;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int r = 4 * (L.i >> 2) + q;
+    L.xoff[q] = (row0 + r < p.B ? r : p.B - 1 - row0) * (int)p.ldx + 32 * L.g + 8 * (L.i & 3);
+  }
 
   // the first full bf16 step's x, scales and reciprocals are requested before the per-tensor
   // maximum is read, so that the two memory round trips overlap
-  const int kfull = p.x_vec_ok ? p.M : 0;
+  // (the quad loads' 32-bit offsets need 17 row strides to fit in an int)
+  const int kfull = (p.x_vec_ok && p.ldx <= (int64_t)(INT32_MAX / 17)) ? p.M : 0;
   int k0 = kbeg + 128 * wave;
   FullIn<RC> cur;
   const bool full0 = DT::is_bf16 && k0 < kend && k0 + 128 <= kfull;
   if constexpr (DT::is_bf16)
-    if (full0) load_full<RC, LR>(p, xrow, L, k0, cur);
+    if (full0) load_full<RC, LR>(p, xblk, L, k0, cur);
 
   L.sx = 0.f;
   L.ysx = 0.f;
@@ -721,7 +779,7 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
         const bool more = kn < kend && kn + 128 <= kfull;
         if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
         FullIn<RC> nxt;
-        load_full<RC, LR>(p, xrow, L, more ? kn : k0, nxt);
+        load_full<RC, LR>(p, xblk, L, more ? kn : k0, nxt);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
         act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
         k0 = kn;
