@@ -379,6 +379,7 @@ int svdq_linear_bias(const void* x, int64_t B, int64_t M, int64_t ldx, const voi
     g.acodes_tiled = mx_large_accepts(g) ? 1 : 0;
     g.kstages = (int)(d.code_row_bytes() / 128);
   }
+  if (fmt == SVDQ_FMT_MX && B <= 64) g.acodes_tiled = 1;  // the decode GEMM takes every such batch
   p.codes_tiled = g.acodes_tiled;
   tm.begin(1);
   if ((st = hip_status(launch_act_quant(p, fmt, dtype, pl.row_blocks, pl.r_chunks, pl.rchunk, s), "activation quantise launch")))

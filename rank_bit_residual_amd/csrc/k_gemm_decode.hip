@@ -11,7 +11,7 @@
 // SIMD; four waves for batches above 32 rows) split K evenly. Each lane loads its 32-code K
 // block of a weight column straight into registers in the MFMA B layout (every weight byte is
 // used once, so there is no LDS staging); the prepared codes are tiled so that a 16-column
-// step is one contiguous 1 KB load. Eight K steps per batch so that many requests are in
+// step is one contiguous 1 KB load, and so are the activation codes of a 16-row tile. Eight K steps per batch so that many requests are in
 // flight; at 16 rows and K = 8192 each wave's whole share is one batch. Each wave adds its share of
 // the up-projection down L2 (16 rank columns per wave, bf16 MFMAs) to its partial tile; those
 // operands are requested ahead of the residual codes and multiplied while the codes are still
@@ -55,13 +55,16 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
     wsrc[tt] = p.wcodes + mx_code_tile_offset(col, p.kq) + g * 16;  // + 1024 per K step
     wssrc[tt] = p.wscales + mx_scale_tiled_index(col, 0, p.kq);
   }
+  // activation codes: 16-row x 128-code tiles (one contiguous 1 KB per MFMA operand, + 1 KB per
+  // K step) when the activation kernel wrote them so, else row-major (+ 64 bytes per K step)
   const uint8_t* asrc[MT];
   const uint8_t* assrc[MT];
+  const int astep = p.acodes_tiled ? 1024 : 64;
 #pragma unroll
   for (int m = 0; m < MT; m++) {
     int row = 16 * m + i;
     row = row < p.B ? row : p.B - 1;
-    asrc[m] = p.acodes + (int64_t)row * p.lda + g * 16;
+    asrc[m] = p.acodes + (p.acodes_tiled ? ((int64_t)(row >> 4) * p.kq << 10) + (row & 15) * 64 : (int64_t)row * p.lda) + g * 16;
     assrc[m] = p.ascales + mx_scale_tiled_index(row, 0, p.kq);
   }
 
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
       }
 #pragma unroll
       for (int m = 0; m < MT; m++) {
-        bt.av[u][m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)(s + u) * 64);
+        bt.av[u][m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)(s + u) * astep);
         bt.asc[u][m] = *reinterpret_cast<const u32*>(assrc[m] + (int64_t)(s + u) * 256);
       }
     }
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
     }
 #pragma unroll
     for (int m = 0; m < MT; m++) {
-      av[m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)s * 64);
+      av[m] = *reinterpret_cast<const v4i*>(asrc[m] + (int64_t)s * astep);
       asc[m] = *reinterpret_cast<const u32*>(assrc[m] + (int64_t)s * 256);
     }
     step(wv, wsc, av, asc);

@@ -133,10 +133,11 @@ def test_activation_codes_bit_exact_workloads(cid):
 
 def _workspace_codes(ws, B, M, mx):
     """The activation codes at the start of svdq_linear's workspace as [B, Kp/2] bytes:
-    row-major, or for MXFP4 above 64 rows (the large-batch GEMM) 1 KB tiles of 16 rows x 128
-    codes, tile (b / 16, k / 128) at ((b / 16) * Kp / 128 + k / 128) KB."""
+    row-major for INT, and for MXFP4 (both MXFP4 GEMMs; operand arrays past 2 GiB, which take
+    the generic kernel, are not used here) 1 KB tiles of 16 rows x 128 codes, tile
+    (b / 16, k / 128) at ((b / 16) * Kp / 128 + k / 128) KB."""
     row = ((M + 255) // 256 * 256) // 2
-    if mx and B > 64:
+    if mx:
         rows16 = -(-B // 16) * 16
         t = ws[: rows16 * row].cpu().numpy().reshape(rows16 // 16, row // 64, 16, 64)
         return t.transpose(0, 2, 1, 3).reshape(rows16, row)[:B]
@@ -146,8 +147,8 @@ def _workspace_codes(ws, B, M, mx):
 @pytest.mark.parametrize("cid,B,rank", [(2, None, None), (5, None, None), (2, 48, 64), (5, 40, 96), (3, 300, None)])
 def test_linear_workspace_codes_bit_exact(cid, B, rank):
     """The codes svdq_linear itself writes (white-box: its workspace begins with the
-    activation codes, [B, Kp/2] nibbles, row-major or, for the large-batch MXFP4 GEMM, in
-    1 KB tiles of 16 rows x 128 codes) equal the oracle's. At the INT and decode shapes the
+    activation codes, [B, Kp/2] nibbles, row-major for INT or, for MXFP4, in 1 KB tiles of 16
+    rows x 128 codes) equal the oracle's. At the INT and decode shapes the
     activation kernel splits the rank over several blocks and shares the coding between
     them, a path svdq_quantize_activations (one rank chunk) does not take."""
     wl = WORKLOADS[cid]
@@ -932,8 +933,8 @@ def test_two_level_parity_workloads(cid, rows):
 @pytest.mark.parametrize("cid,B,gx", [(5, None, 0.37), (3, 512, 1.37), (3, 100, 9.0)])
 def test_two_level_workspace_codes_bit_exact(cid, B, gx):
     """svdq_linear's activation codes under two-level scaling are the MXFP4 codes of the
-    binary32 products RN(X^ * g_x) (white-box: the workspace begins with them, tiled above 64
-    rows)."""
+    binary32 products RN(X^ * g_x) (white-box: the workspace begins with them, in 16-row
+    tiles)."""
     wl = WORKLOADS[cid]
     x, w, s = make_inputs(cid, B=B)
     p = R.prepare(_g(w, wl.dtype), torch.from_numpy(s), wl.rank, 4, "mx", x_global_scale=gx)
