@@ -184,6 +184,11 @@ __device__ inline void unpack_nibbles(u32 w, u32& lo, u32& hi) {
 }
 
 // ---- the down-projection operand of the GEMM epilogues -----------------------------------
+// Split-K partials of down are stored per chunk in groups of 16 rank columns: chunk c holds
+// [rp / 16][B][16] f32, so the entries (row, k) of one 16-column group for consecutive rows are
+// contiguous (a wave reading 16 rows x 16 columns reads one kilobyte). Chunks are B * rp apart.
+__device__ inline int64_t part_index(int B, int row, int k) { return ((int64_t)(k >> 4) * B + row) * 16 + (k & 15); }
+
 // Eight consecutive entries down[row][k .. k+8) as bf16 (the operand of the up-projection
 // MFMAs): read directly, or, when the activation kernel split K over `chunks` blocks, the sum
 // of the f32 partials in chunk order 0, 1, ..., rounded once to bf16 (the same value the
@@ -193,7 +198,7 @@ __device__ inline v8bf down8_bf16_pf(const void* down, const float* part, int ch
   if (chunks <= 1)
     return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(down) +
                                                                    (int64_t)row * rp + k));
-  const float* src = part + (int64_t)row * rp + k;
+  const float* src = part + part_index(B, row, k);  // k % 16 is 0 or 8: the eight entries are contiguous
   const int64_t stride = (int64_t)B * rp;
   // the first PF chunks are requested together (indices past the last chunk reload the last
   // one and are not added), the rest one after another; the sum runs in chunk order
@@ -225,7 +230,7 @@ __device__ inline v8bf down8_bf16(const void* down, const float* part, int chunk
 // One entry down[row][k] as f32 (f32 io): direct, or the ordered sum of the partials.
 __device__ inline float down1_f32(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
   if (chunks <= 1) return reinterpret_cast<const float*>(down)[(int64_t)row * rp + k];
-  const float* src = part + (int64_t)row * rp + k;
+  const float* src = part + part_index(B, row, k);
   float s = src[0];
   for (int c = 1; c < chunks; c++) s += src[(int64_t)c * B * rp];
   return s;

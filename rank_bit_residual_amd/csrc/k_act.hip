@@ -811,7 +811,7 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
         if (p.k_chunks == 1)
           reinterpret_cast<T*>(p.down)[(int64_t)bb * p.rp + L.rbase + c] = DT::from_f32(s);
         else
-          p.down_part[((int64_t)blockIdx.y * p.B + bb) * p.rp + L.rbase + c] = s;
+          p.down_part[(int64_t)blockIdx.y * p.B * p.rp + part_index(p.B, bb, L.rbase + c)] = s;
       }
     }
   }

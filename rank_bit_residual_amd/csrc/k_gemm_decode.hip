@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
 #pragma unroll
         for (int c = 0; c < PF; c++)
           if (c < p.down_chunks)
-            u.part[m][c] = *reinterpret_cast<const v4f*>(p.down_part + c * stride + (int64_t)urow[m] * p.rp + kk);
+            u.part[m][c] = *reinterpret_cast<const v4f*>(p.down_part + c * stride + part_index(p.B, urow[m], kk));
     }
   };
   auto up_mma = [&](const UpOps& u, int kk) {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_gemm_decode_mx(GemmParams p)
           if (c < p.down_chunks) sum += u.part[m][c];
         const int64_t stride = (int64_t)p.B * p.rp;
         for (int c = PF; c < p.down_chunks; c++)
-          sum += *reinterpret_cast<const v4f*>(p.down_part + c * stride + (int64_t)urow[m] * p.rp + kk);
+          sum += *reinterpret_cast<const v4f*>(p.down_part + c * stride + part_index(p.B, urow[m], kk));
         if constexpr (DT::is_bf16) {
           const u32 lo = pack_bf16x2(sum[0], sum[1]), hi = pack_bf16x2(sum[2], sum[3]);
           a = __builtin_bit_cast(v4s, v2u{lo, hi});

@@ -29,7 +29,7 @@ struct ActParams {
   float* sx_out;  // INT: receives s_x (may be NULL)
   const void* l1t;  // [rp][Kp] dtype
   int rp;
-  float* down_part;  // [k_chunks][B][rp] f32 when k_chunks > 1
+  float* down_part;  // [k_chunks][rp / 16][B][16] f32 when k_chunks > 1 (part_index)
   void* down;        // [B][rp] dtype when k_chunks == 1
   int k_chunks, k_chunk_len;
   int x_vec_ok;  // x base and row stride allow 16-byte loads
@@ -49,7 +49,7 @@ struct GemmParams {
   const float* sx;
   const float* sr;
   const void* down;         // [B][rp] dtype, when down_chunks == 1
-  const float* down_part;   // [down_chunks][B][rp] f32 split-K partials of X^ L1, when down_chunks > 1
+  const float* down_part;   // [down_chunks][rp / 16][B][16] f32 split-K partials of X^ L1 (part_index), when down_chunks > 1
   int down_chunks;
   const void* l2t;
   int rp;
