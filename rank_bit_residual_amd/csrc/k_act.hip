@@ -753,9 +753,20 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   L.qmax = 0.f;
   L.gx = (FMT == SVDQ_FMT_MX && p.gscale) ? p.gscale[0] : 1.f;
   if constexpr (FMT == SVDQ_FMT_INT) {
-    // each wave reduces the partial maxima on its own (an exact max, so all waves agree)
+    // each wave reduces the partial maxima on its own (an exact max, so all waves agree), eight
+    // loads per lane issued together per 512 partials (one memory round trip instead of one
+    // per 64); indices past the last partial re-read it, which leaves the maximum unchanged
     float a = 0.f;
-    for (int q = L.lane; q < p.n_amax; q += 64) a = fmaxf(a, p.amax_part[q]);
+    for (int q0 = 0; q0 < p.n_amax; q0 += 512) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int q = q0 + 64 * u + L.lane;
+        v[u] = p.amax_part[q < p.n_amax ? q : p.n_amax - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) a = fmaxf(a, v[u]);
+    }
     const float amax = wave_max(a);
     L.qmax = (float)((1 << (p.bits - 1)) - 1);
     L.sx = amax / L.qmax;
