@@ -584,6 +584,25 @@ def test_strided_activations_match_contiguous():
     assert torch.equal(R.linear(big[:, 16:16 + 3072], p), R.linear(_g(x, "bf16"), p))
 
 
+@pytest.mark.parametrize("fmt", ["mx", "int"])
+def test_activation_row_stride_past_quad_offsets(fmt):
+    """Full activation steps load x by quads with 32-bit element offsets spanning 17 row
+    strides; a row stride above INT32_MAX / 17 elements takes the per-lane loads instead. Two
+    rows 130 M elements apart (a 260 MB view) give the same output as their contiguous copy."""
+    x, w, s = make_inputs(3, B=2)
+    p = R.prepare(_g(w, "bf16"), torch.from_numpy(s), 32, 4, fmt)
+    ldx, M = 130_000_000, x.shape[1]
+    assert ldx > (2**31 - 1) // 17 and ldx % 8 == 0
+    big = torch.zeros(ldx + M, dtype=torch.bfloat16, device=dev())
+    view = big.as_strided((2, M), (ldx, 1))
+    view.copy_(_g(x, "bf16"))
+    got = R.linear(view, p)
+    want = R.linear(_g(x, "bf16"), p)
+    torch.cuda.synchronize()
+    del big, view
+    assert torch.equal(got, want)
+
+
 # ----------------------------------------------------------------------------- large-batch MXFP4 kernel
 def _mx_case(B, M, N, rank, seed):
     rng = np.random.default_rng(seed)
