@@ -193,29 +193,46 @@ __device__ inline int64_t part_index(int B, int row, int k) { return ((int64_t)(
 // MFMAs): read directly, or, when the activation kernel split K over `chunks` blocks, the sum
 // of the f32 partials in chunk order 0, 1, ..., rounded once to bf16 (the same value the
 // unsplit kernel would store).
+// The operands of down8_bf16_pf, requested by down8_request and summed by down8_sum, so that a
+// caller can put other work (or other requests) between the two.
 template <int PF>
-__device__ inline v8bf down8_bf16_pf(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
-  if (chunks <= 1)
-    return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(down) +
-                                                                   (int64_t)row * rp + k));
+struct Down8Raw {
+  float4 lo[PF], hi[PF];
+};
+
+template <int PF>
+__device__ inline void down8_request(const void* down, const float* part, int chunks, int B, int rp, int row, int k,
+                                     Down8Raw<PF>& r) {
+  if (chunks <= 1) {  // the eight bf16 entries, as bits
+    r.lo[0] = *reinterpret_cast<const float4*>(reinterpret_cast<const uint16_t*>(down) + (int64_t)row * rp + k);
+    return;
+  }
   const float* src = part + part_index(B, row, k);  // k % 16 is 0 or 8: the eight entries are contiguous
   const int64_t stride = (int64_t)B * rp;
-  // the first PF chunks are requested together (indices past the last chunk reload the last
-  // one and are not added), the rest one after another; the sum runs in chunk order
-  float4 lo[PF], hi[PF];
+  // the first PF chunks are requested together (indices past the last chunk reload the last one)
 #pragma unroll
   for (int c = 0; c < PF; c++) {
     const int cc = c < chunks ? c : chunks - 1;
-    lo[c] = *reinterpret_cast<const float4*>(src + cc * stride);
-    hi[c] = *reinterpret_cast<const float4*>(src + cc * stride + 4);
+    r.lo[c] = *reinterpret_cast<const float4*>(src + cc * stride);
+    r.hi[c] = *reinterpret_cast<const float4*>(src + cc * stride + 4);
   }
-  float s[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, hi[0].x, hi[0].y, hi[0].z, hi[0].w};
+}
+
+// The sum runs in chunk order; chunks past PF are loaded one after another. A requested chunk
+// past the last adds -0.0, which leaves every sum unchanged, so the adds need no branch (a
+// branch per chunk let the compiler sink that chunk's loads behind the waits for the others).
+template <int PF>
+__device__ inline v8bf down8_sum(const Down8Raw<PF>& r, const float* part, int chunks, int B, int rp, int row, int k) {
+  if (chunks <= 1) return __builtin_bit_cast(v8bf, r.lo[0]);
+  float s[8] = {r.lo[0].x, r.lo[0].y, r.lo[0].z, r.lo[0].w, r.hi[0].x, r.hi[0].y, r.hi[0].z, r.hi[0].w};
 #pragma unroll
-  for (int c = 1; c < PF; c++)
-    if (c < chunks) {
-      s[0] += lo[c].x; s[1] += lo[c].y; s[2] += lo[c].z; s[3] += lo[c].w;
-      s[4] += hi[c].x; s[5] += hi[c].y; s[6] += hi[c].z; s[7] += hi[c].w;
-    }
+  for (int c = 1; c < PF; c++) {
+    const bool on = c < chunks;
+    s[0] += on ? r.lo[c].x : -0.0f; s[1] += on ? r.lo[c].y : -0.0f; s[2] += on ? r.lo[c].z : -0.0f; s[3] += on ? r.lo[c].w : -0.0f;
+    s[4] += on ? r.hi[c].x : -0.0f; s[5] += on ? r.hi[c].y : -0.0f; s[6] += on ? r.hi[c].z : -0.0f; s[7] += on ? r.hi[c].w : -0.0f;
+  }
+  const float* src = part + part_index(B, row, k);
+  const int64_t stride = (int64_t)B * rp;
   for (int c = PF; c < chunks; c++) {
     const float4 a = *reinterpret_cast<const float4*>(src + c * stride), b = *reinterpret_cast<const float4*>(src + c * stride + 4);
     s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w; s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
@@ -223,6 +240,14 @@ __device__ inline v8bf down8_bf16_pf(const void* down, const float* part, int ch
   return __builtin_bit_cast(v8bf, v4i{(int)pack_bf16x2(s[0], s[1]), (int)pack_bf16x2(s[2], s[3]),
                                       (int)pack_bf16x2(s[4], s[5]), (int)pack_bf16x2(s[6], s[7])});
 }
+
+template <int PF>
+__device__ inline v8bf down8_bf16_pf(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
+  Down8Raw<PF> r;
+  down8_request<PF>(down, part, chunks, B, rp, row, k, r);
+  return down8_sum<PF>(r, part, chunks, B, rp, row, k);
+}
+
 __device__ inline v8bf down8_bf16(const void* down, const float* part, int chunks, int B, int rp, int row, int k) {
   return down8_bf16_pf<1>(down, part, chunks, B, rp, row, k);
 }

@@ -279,13 +279,14 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
   const int bcol = col < p.npad ? col : p.npad - 1;
   const T* l2t = reinterpret_cast<const T*>(p.l2t);
   constexpr int RMAX = 4;
-  v8bf ua[RMAX], ub[RMAX];
+  v8bf ub[RMAX];
+  Down8Raw<4> ur[RMAX];  // down's entries or split-K partials, summed after the exchange
   float fa[2 * RMAX], fb[2 * RMAX];
   if constexpr (DT::is_bf16) {
 #pragma unroll
     for (int r = 0; r < RMAX; r++)
       if (16 * r < p.rp) {
-        ua[r] = down8_bf16_pf<4>(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g);
+        down8_request<4>(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g, ur[r]);
         ub[r] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + 16 * r + 8 * g));
       }
   } else {
@@ -297,8 +298,10 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
       }
   }
 
-  // ---- exact sum of the four waves' partial tiles; wave q then owns quadrant q
-  __syncthreads();
+  // ---- exact sum of the four waves' partial tiles; wave q then owns quadrant q. The ring's
+  // stages have all been waited for and read, so LDS-only barriers suffice and the epilogue
+  // operands requested above stay in flight across the exchange.
+  lds_barrier();
   v4i* part = reinterpret_cast<v4i*>(smem);  // [wave][tile][v/4][lane] of 4 int32
 #pragma unroll
   for (int i = 0; i < 2; i++)
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
       for (int v4 = 0; v4 < 4; v4++)
         part[((wave * 4 + 2 * i + j) * 4 + v4) * 64 + lane] =
             v4i{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
-  __syncthreads();
+  lds_barrier();
   v16f f;
   const float scl = p.sx[0] * p.sr[0];
 #pragma unroll
@@ -325,7 +328,9 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmParams p) {
     if constexpr (DT::is_bf16) {
 #pragma unroll
       for (int r = 0; r < RMAX; r++)
-        if (16 * r < p.rp) f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[r], ub[r], f, 0, 0, 0);
+        if (16 * r < p.rp)
+          f = __builtin_amdgcn_mfma_f32_32x32x16_bf16(down8_sum<4>(ur[r], p.down_part, p.down_chunks, p.B, p.rp, erow, 16 * r + 8 * g),
+                                                      ub[r], f, 0, 0, 0);
       for (int kk = 16 * RMAX; kk < p.rp; kk += 16) {
         const v8bf av = down8_bf16(p.down, p.down_part, p.down_chunks, p.B, p.rp, erow, kk + 8 * g);
         const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(l2t + (int64_t)bcol * p.rp + kk + 8 * g));
