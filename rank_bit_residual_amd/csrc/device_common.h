@@ -269,6 +269,15 @@ __device__ inline float bias_at(const void* bias, int col, int N) {
   return DT::to_f32(reinterpret_cast<const typename DT::T*>(bias)[col < N ? col : N - 1]);
 }
 
+// A workgroup barrier for LDS hand-offs only: the wave's own LDS operations complete
+// (lgkmcnt(0)), then s_barrier. Unlike __syncthreads it does not wait for outstanding global
+// loads and stores (vmcnt counts both), so those stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- wave / block reductions ------------------------------------------------------------
 __device__ inline float wave_max(float v) {
 #pragma unroll

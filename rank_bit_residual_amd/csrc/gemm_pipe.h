@@ -26,15 +26,6 @@ __device__ __forceinline__ void buffer_to_lds4(const uint8_t* array, int bytes, 
                                            (lds_ptr_t)lds, 4, voffset, soffset, 0, 0);
 }
 
-// A workgroup barrier for LDS hand-offs only: the wave's own LDS operations complete
-// (lgkmcnt(0)), then s_barrier. Unlike __syncthreads it does not wait for outstanding global
-// loads, so requests issued before it stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // s_waitcnt vmcnt(n) for a compile-time n (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ inline void wait_vmcnt() {
