@@ -705,8 +705,9 @@ __device__ __forceinline__ void act_step(const ActParams& p, const typename DT::
   act_finish<DT, FMT, NIB, RC>(p, L, k0, acc, st);
 }
 
-// LR: the block has low-rank columns (rank > 0; then every block has at least one 16-wide tile)
-template <class DT, int FMT, bool NIB, int RC, bool LR>
+// LR: the block has low-rank columns (rank > 0; then every block has at least one 16-wide tile).
+// ONE: K chunks of at most one step per wave (decode and small batches), so no wave prefetches.
+template <class DT, int FMT, bool NIB, int RC, bool LR, bool ONE>
 __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   typedef typename DT::T T;
   constexpr int NW = ACT_WAVES;
@@ -784,7 +785,15 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   // compiler's wait for the current step's operands leaves them in flight.
   v4i bwc[RC / 16][4];  // the current full step's L1^T operands when they do not travel ahead
   if constexpr (DT::is_bf16) {
-    if (full0) {
+    // ONE: a wave with a single full step takes it without a prefetch. The general loop stays
+    // in that instantiation as the other branch (measured faster at decode than without it);
+    // other instantiations compile the loop alone.
+    const int kn0 = k0 + 128 * NW;
+    if (ONE && full0 && !(kn0 < kend && kn0 + 128 <= kfull)) {
+      if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);
+      act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
+      k0 = kn0;
+    } else if (full0) {
       for (;;) {
         const int kn = k0 + 128 * NW;
         const bool more = kn < kend && kn + 128 <= kfull;
@@ -919,16 +928,22 @@ hipError_t launch_act_quant(const ActParams& p, int fmt, int dtype, int row_bloc
   const dim3 grid(row_blocks, p.k_chunks, r_chunks);
   const int threads = 64 * ACT_WAVES;
   const bool nib = fmt == SVDQ_FMT_MX || p.bits <= 4;
-#define SVDQ_ACT(DT, FMT, NIB)                                             \
-  do {                                                                      \
-    if (p.rp == 0)                                                          \
-      k_act_quant<DT, FMT, NIB, 16, false><<<grid, threads, 0, stream>>>(p); \
-    else if (rchunk == 16)                                                  \
-      k_act_quant<DT, FMT, NIB, 16, true><<<grid, threads, 0, stream>>>(p);  \
-    else if (rchunk == 32)                                                  \
-      k_act_quant<DT, FMT, NIB, 32, true><<<grid, threads, 0, stream>>>(p);  \
-    else                                                                    \
-      k_act_quant<DT, FMT, NIB, 64, true><<<grid, threads, 0, stream>>>(p);  \
+  // at most one K step per wave (K chunks of up to 128 x waves): the bf16 form without prefetch
+  const bool one = dtype == SVDQ_BF16 && p.k_chunk_len <= 128 * ACT_WAVES;
+#define SVDQ_ACT(DT, FMT, NIB)                                                    \
+  do {                                                                             \
+    if (p.rp == 0 && one)                                                          \
+      k_act_quant<DT, FMT, NIB, 16, false, true><<<grid, threads, 0, stream>>>(p);  \
+    else if (p.rp == 0)                                                            \
+      k_act_quant<DT, FMT, NIB, 16, false, false><<<grid, threads, 0, stream>>>(p); \
+    else if (rchunk == 16 && one)                                                  \
+      k_act_quant<DT, FMT, NIB, 16, true, true><<<grid, threads, 0, stream>>>(p);   \
+    else if (rchunk == 16)                                                         \
+      k_act_quant<DT, FMT, NIB, 16, true, false><<<grid, threads, 0, stream>>>(p);  \
+    else if (rchunk == 32)                                                         \
+      k_act_quant<DT, FMT, NIB, 32, true, false><<<grid, threads, 0, stream>>>(p);  \
+    else                                                                           \
+      k_act_quant<DT, FMT, NIB, 64, true, false><<<grid, threads, 0, stream>>>(p);  \
   } while (0)
   if (!p.recip || (rchunk != 16 && rchunk != 32 && rchunk != 64)) return hipErrorInvalidValue;
   if (dtype == SVDQ_BF16) {
