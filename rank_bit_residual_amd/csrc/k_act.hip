@@ -780,9 +780,9 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
   for (int n = 0; n < RC / 16; n++) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // full steps first (k0 ascending), then the tail and padding; bf16 full steps load the next
-  // step's x and reciprocals before computing the current one. Those loads are issued whether
-  // or not a next step exists (the last step reloads its own columns, unused), so that the
-  // compiler's wait for the current step's operands leaves them in flight.
+  // step's x and reciprocals before computing the current one (a fixed set of loads, so that the
+  // compiler's wait for the current step's operands leaves them in flight); a wave's last full
+  // step has nothing to prefetch and takes its own copy of the step.
   v4i bwc[RC / 16][4];  // the current full step's L1^T operands when they do not travel ahead
   if constexpr (DT::is_bf16) {
     // ONE: a wave with a single full step takes it without a prefetch. The general loop stays
@@ -798,12 +798,16 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
         const int kn = k0 + 128 * NW;
         const bool more = kn < kend && kn + 128 <= kfull;
         if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
+        if (!more) {  // the wave's last full step: nothing to prefetch
+          act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
+          k0 = kn;
+          break;
+        }
         FullIn<RC> nxt;
-        load_full<RC, LR>(p, xblk, L, more ? kn : k0, nxt);
+        load_full<RC, LR>(p, xblk, L, kn, nxt);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
         act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
         k0 = kn;
-        if (!more) break;
         cur = nxt;
       }
     }
