@@ -309,8 +309,9 @@ constexpr bool l1_ahead(int RC) { return RC <= 32; }
 
 // Inputs of a full bf16 step that the caller loads one step ahead: 16 words of bf16 x pairs as
 // the quad loads left them (quad_transpose turns them into the lane's own 32 values), two
-// reciprocals and two scales, and (l1_ahead) the step's L1^T operands. Lane l = 16 g + q holds RN(1/s) and s of columns k0 + 2 l and k0 + 2 l + 1, i.e. the
-// pair q of the block that the lanes of row g work on.
+// reciprocals and two scales, and (l1_ahead) the step's L1^T operands. Lane l = 16 g + q holds
+// RN(1/s) and s of columns k0 + 2 l and k0 + 2 l + 1, i.e. the pair q of the block that the
+// lanes of row g work on.
 template <int RC>
 struct FullIn {
   u32 raw[16];
