@@ -795,21 +795,45 @@ __global__ __launch_bounds__(512) void k_act_quant(ActParams p) {
       act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
       k0 = kn0;
     } else if (full0) {
-      for (;;) {
-        const int kn = k0 + 128 * NW;
-        const bool more = kn < kend && kn + 128 <= kfull;
-        if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
-        if (!more) {  // the wave's last full step: nothing to prefetch
+      if constexpr (!ONE) {
+        // two alternating buffers: the step after next is requested before the wait for the next
+        FullIn<RC> nxt;
+        // one step: compute from `a` after requesting the next step into `b` (none after the last)
+        auto one = [&](FullIn<RC>& a, FullIn<RC>& b) -> bool {
+          const int kn = k0 + 128 * NW;
+          const bool more = kn < kend && kn + 128 <= kfull;
+          if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
+          if (!more) {
+            act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, a, bwc);
+            k0 = kn;
+            return false;
+          }
+          load_full<RC, LR>(p, xblk, L, kn, b);
+          __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
+          act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, a, bwc);
+          k0 = kn;
+          return true;
+        };
+        while (one(cur, nxt) && one(nxt, cur)) {
+        }
+      } else {
+        // (the ONE instantiation's fallback keeps the single-buffer loop: measured faster there)
+        for (;;) {
+          const int kn = k0 + 128 * NW;
+          const bool more = kn < kend && kn + 128 <= kfull;
+          if constexpr (!l1_ahead(RC) && LR) load_l1_all<RC, T>(p, L, k0, bwc);  // before the next step's x
+          if (!more) {  // the wave's last full step: nothing to prefetch
+            act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
+            k0 = kn;
+            break;
+          }
+          FullIn<RC> nxt;
+          load_full<RC, LR>(p, xblk, L, kn, nxt);
+          __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
           act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
           k0 = kn;
-          break;
+          cur = nxt;
         }
-        FullIn<RC> nxt;
-        load_full<RC, LR>(p, xblk, L, kn, nxt);
-        __builtin_amdgcn_sched_barrier(0);  // the prefetch goes out before any wait on this step's data
-        act_step<DT, FMT, NIB, true, RC>(p, xrow, L, k0, acc, cur, bwc);
-        k0 = kn;
-        cur = nxt;
       }
     }
   } else {
